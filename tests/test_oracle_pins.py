@@ -1,0 +1,287 @@
+"""Pins the float64 oracle to things other than itself.
+
+Each test ties the token-loop oracle to a value printed on the pages, a closed
+form, an independent algorithm (brute force, the chunked UT form) or an
+invariant, chosen so that a dropped term, a wrong sign or index, or a
+transposed operand in the oracle fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute, chunk_form
+from tests.conftest import read_golden
+
+
+def _rand_unit(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return x / np.sqrt((x * x).sum(-1, keepdims=True) + 1e-6)
+
+
+def _rand_seq(rng, L, Dk, Dv, gate=True, gk=False, s0=True):
+    q = _rand_unit(rng, L, Dk)
+    k = _rand_unit(rng, L, Dk)
+    v = rng.standard_normal((L, Dv))
+    beta = 1 / (1 + np.exp(-rng.standard_normal(L)))
+    g = -np.exp(rng.uniform(-2, 1)) * np.log1p(np.exp(rng.standard_normal(L) + rng.uniform(-1, 1))) if gate else None
+    gkv = rng.uniform(-0.5, -0.001, (L, Dk)) if gk else None
+    S0 = rng.standard_normal((Dk, Dv)) * 0.3 if s0 else None
+    return q, k, v, beta, g, gkv, S0
+
+
+# --- values printed on the deltanet.rs page ---------------------------------
+
+def test_hand_computed_step():
+    f = read_golden("deltanet_rs_hand_step.txt")
+    S0 = np.array(f["S0"]).reshape(2, 2)
+    out, S = oracle.sequence(np.array([f["q"]]), np.array([f["k"]]), np.array([f["v"]]),
+                             np.array(f["beta"]), g=np.array(f["g"]), state=S0,
+                             scale=f["scale"][0])
+    np.testing.assert_allclose(out[0], f["out"], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(S.reshape(-1), f["S"], atol=1e-12, rtol=0)
+
+
+def test_decay_applies_before_read():
+    f = read_golden("deltanet_rs_decay_first.txt")
+    S0 = np.array(f["S0"]).reshape(2, 2)
+    out, S = oracle.sequence(np.array([f["q"]]), np.array([f["k"]]), np.array([f["v"]]),
+                             np.array(f["beta"]), g=np.array(f["g"]), state=S0,
+                             scale=f["scale"][0])
+    assert abs(out[0, 0] - f["out0"][0]) < 1e-12
+    assert abs(S[0, 0] - f["S00"][0]) < 1e-12
+    # A read before the decay would give kv = 2, delta = -1, S[0,0] = 0: a different answer.
+    assert abs(S[0, 0]) > 0.5
+
+
+def test_beta_one_is_pure_delta_rule_closed_form():
+    f = read_golden("deltanet_rs_beta_one.txt")
+    Dk, Dv = int(f["Dk"][0]), int(f["Dv"][0])
+    S0 = np.array([((n * 37 % 11) - 5) * 0.1 for n in range(Dk * Dv)]).reshape(Dk, Dv)
+    k = np.array(f["k_raw"])
+    k = k / math.sqrt((k * k).sum() + 1e-6)
+    v = np.array(f["v"])
+    _, S = oracle.sequence(np.array([f["q"]]), k[None], v[None], np.array(f["beta"]),
+                           g=np.array(f["g"]), state=S0, scale=1.0)
+    expect = S0 - np.outer(k, k @ S0) + np.outer(k, v)
+    np.testing.assert_allclose(S, expect, atol=1e-12, rtol=0)
+    assert np.abs(S - expect).max() < f["tolerance_on_page"][0]
+
+
+def test_retention_at_g_minus_one():
+    # The decode operator page: g = -1 keeps about 37 % of the state per step.
+    S0 = np.eye(3)
+    _, S = oracle.sequence(np.zeros((1, 3)), np.zeros((1, 3)), np.zeros((1, 3)),
+                           np.zeros(1), g=np.array([-1.0]), state=S0)
+    assert abs(S[0, 0] - 0.36787944117144233) < 1e-15
+    assert round(S[0, 0], 2) == 0.37
+
+
+# --- (a) brute force: explicit transition-matrix products --------------------
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("gk", [False, True])
+def test_brute_force_unrolled(seed, gk):
+    rng = np.random.default_rng(1000 + seed)
+    L = int(rng.integers(1, 7))
+    Dk = int(rng.integers(1, 5))
+    Dv = int(rng.integers(1, 5))
+    q, k, v, beta, g, gkv, S0 = _rand_seq(rng, L, Dk, Dv, gate=seed % 3 != 0, gk=gk, s0=seed % 2 == 0)
+    scale = 0.7
+    out, S = oracle.sequence(q, k, v, beta, g=g, gk=gkv, state=S0, scale=scale)
+    out_b, states_b = brute.unrolled(q, k, v, beta, g, gkv, S0, scale)
+    np.testing.assert_allclose(out, out_b, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(S, states_b[-1], atol=1e-12, rtol=0)
+
+
+# --- (b) store then recall with orthonormal keys -----------------------------
+
+@pytest.mark.parametrize("Dk,n,rewrite", [(8, 6, 2), (16, 16, 5), (5, 3, 3)])
+def test_store_then_recall(Dk, n, rewrite):
+    rng = np.random.default_rng(Dk * 100 + n)
+    Dv = 7
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    keys = Qm.T[:n]                         # n orthonormal rows
+    vals = rng.standard_normal((n, Dv))
+    new_vals = rng.standard_normal((rewrite, Dv))
+    # Tokens: write all n pairs (each query recalls a random earlier key), then rewrite
+    # the first `rewrite` keys, then read every key once with beta = 0.
+    ks, vs, bs, qs, want = [], [], [], [], []
+    for t in range(n):
+        j = int(rng.integers(0, t + 1))
+        ks.append(keys[t]); vs.append(vals[t]); bs.append(1.0); qs.append(keys[j]); want.append(vals[j])
+    cur = vals.copy()
+    for i in range(rewrite):
+        cur[i] = new_vals[i]
+        ks.append(keys[i]); vs.append(new_vals[i]); bs.append(1.0); qs.append(keys[i]); want.append(new_vals[i])
+    for j in range(n):
+        ks.append(keys[j]); vs.append(np.zeros(Dv)); bs.append(0.0); qs.append(keys[j]); want.append(cur[j])
+    out, S = oracle.sequence(np.array(qs), np.array(ks), np.array(vs), np.array(bs),
+                             g=np.zeros(len(ks)), state=None, scale=1.0)
+    np.testing.assert_allclose(out, np.array(want), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(S.T @ keys.T, cur.T, atol=1e-12, rtol=0)
+
+
+# --- (c) chunked == recurrent ------------------------------------------------
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("gate", [True, False])
+def test_chunked_equals_recurrent(C, gate):
+    rng = np.random.default_rng(C * 7 + gate)
+    for L, Dk, Dv, s0 in [(150, 16, 12, True), (64, 8, 8, False), (37, 32, 16, True), (5, 4, 4, True)]:
+        q, k, v, beta, g, _, S0 = _rand_seq(rng, L, Dk, Dv, gate=gate, s0=s0)
+        out, S = oracle.sequence(q, k, v, beta, g=g, state=S0, scale=0.3)
+        out_c, S_c = chunk_form.chunked(q, k, v, beta, g, S0, 0.3, chunk=C)
+        tol_o = 1e-10 * max(1.0, np.abs(out).max())
+        tol_s = 1e-10 * max(1.0, np.abs(S).max())
+        assert np.abs(out - out_c).max() <= tol_o
+        assert np.abs(S - S_c).max() <= tol_s
+
+
+def test_chunked_equals_recurrent_strong_decay():
+    # Large negative log decays (gamma over a chunk in the hundreds): log-space ratios.
+    rng = np.random.default_rng(99)
+    L, Dk, Dv = 130, 16, 16
+    q, k, v, beta, _, _, S0 = _rand_seq(rng, L, Dk, Dv)
+    g = -rng.uniform(0.0, 10.0, L)
+    out, S = oracle.sequence(q, k, v, beta, g=g, state=S0, scale=1.0)
+    out_c, S_c = chunk_form.chunked(q, k, v, beta, g, S0, 1.0, chunk=64)
+    assert np.isfinite(out_c).all() and np.isfinite(S_c).all()
+    assert np.abs(out - out_c).max() <= 1e-10 * max(1, np.abs(out).max())
+    assert np.abs(S - S_c).max() <= 1e-10 * max(1, np.abs(S).max())
+
+
+# --- (d) g absent == alpha 1 -------------------------------------------------
+
+def test_g_absent_is_bitwise_g_zero():
+    rng = np.random.default_rng(5)
+    B, Nk, Nv, S, D = 2, 1, 2, 9, 8
+    q = _rand_unit(rng, B * Nk * S, D).reshape(B, Nk, S, D)
+    k = _rand_unit(rng, B * Nk * S, D).reshape(B, Nk, S, D)
+    v = rng.standard_normal((B, Nv, S, D))
+    beta = rng.uniform(0, 1, (B, Nv, S))
+    init = rng.standard_normal((B, Nv, D, D))
+    o1, f1 = oracle.prefill(q, k, v, beta, None, init, [9, 4], 0.5)
+    o2, f2 = oracle.prefill(q, k, v, beta, np.zeros((B, Nv, S)), init, [9, 4], 0.5)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    # and with a nonzero g the results differ
+    o3, _ = oracle.prefill(q, k, v, beta, np.full((B, Nv, S), -0.1), init, [9, 4], 0.5)
+    assert not np.array_equal(o1, o3)
+
+
+# --- closed forms and reductions ---------------------------------------------
+
+def test_pure_decay_closed_form():
+    rng = np.random.default_rng(11)
+    L, Dk, Dv = 6, 5, 3
+    q, k, v, _, g, gk, S0 = _rand_seq(rng, L, Dk, Dv, gk=True)
+    _, S = oracle.sequence(q, k, v, np.zeros(L), g=g, gk=gk, state=S0)
+    expect = math.exp(g.sum()) * np.exp(gk.sum(0))[:, None] * S0
+    np.testing.assert_allclose(S, expect, atol=1e-13, rtol=0)
+
+
+def test_orthogonal_keys_reduce_to_decayed_linear_attention():
+    # With mutually orthogonal keys and a zero entering state the memory read is
+    # always zero, so the recurrence is gated linear attention with keys beta_t k_t
+    # (ssm_lab.py, linear_attention_parallel with per-step decays):
+    #   O = scale * ((Q (beta K)^T) * M) V,  M[t,s] = prod_{s<j<=t} alpha_j (s <= t).
+    rng = np.random.default_rng(12)
+    Dk, Dv, L = 12, 5, 9
+    Qm, _ = np.linalg.qr(rng.standard_normal((Dk, Dk)))
+    k = Qm.T[:L]
+    q = _rand_unit(rng, L, Dk)
+    v = rng.standard_normal((L, Dv))
+    beta = rng.uniform(0.1, 1.0, L)
+    g = -rng.uniform(0.01, 1.0, L)
+    out, _ = oracle.sequence(q, k, v, beta, g=g, scale=0.6)
+    logc = np.cumsum(g)
+    M = np.zeros((L, L))
+    for t in range(L):
+        for s in range(t + 1):
+            M[t, s] = math.exp(logc[t] - logc[s])
+    expect = 0.6 * ((q @ (beta[:, None] * k).T) * M) @ v
+    np.testing.assert_allclose(out, expect, atol=1e-12, rtol=0)
+
+
+def test_axis_keys_with_per_key_gate_reduce_to_linear_attention():
+    # Standard-basis keys stay orthogonal under the per-key decay, so the same
+    # reduction holds with a decay per key coordinate.
+    rng = np.random.default_rng(13)
+    Dk, Dv, L = 6, 4, 6
+    perm = rng.permutation(Dk)[:L]
+    k = np.eye(Dk)[perm]
+    q = _rand_unit(rng, L, Dk)
+    v = rng.standard_normal((L, Dv))
+    beta = rng.uniform(0.1, 1.0, L)
+    g = -rng.uniform(0.01, 0.5, L)
+    gk = -rng.uniform(0.001, 0.5, (L, Dk))
+    out, _ = oracle.sequence(q, k, v, beta, g=g, gk=gk, scale=1.0)
+    expect = np.zeros((L, Dv))
+    for t in range(L):
+        for s in range(t + 1):
+            i = perm[s]
+            dec = math.exp(sum(g[s + 1:t + 1]) + sum(gk[s + 1:t + 1, i]))
+            expect[t] += q[t, i] * beta[s] * dec * v[s]
+    np.testing.assert_allclose(out, expect, atol=1e-12, rtol=0)
+
+
+def test_dk1_is_an_ema():
+    rng = np.random.default_rng(14)
+    L, Dv = 20, 3
+    k = rng.choice([-1.0, 1.0], L)[:, None]
+    q = rng.choice([-1.0, 1.0], L)[:, None]
+    v = rng.standard_normal((L, Dv))
+    beta = rng.uniform(0, 1, L)
+    g = -rng.uniform(0, 1, L)
+    s0 = rng.standard_normal((1, Dv))
+    out, S = oracle.sequence(q, k, v, beta, g=g, state=s0, scale=1.0)
+    # closed form: S_t = P_t s0 + sum_i (P_t / P_i) beta_i k_i v_i, P_t = prod_{j<=t} alpha_j (1 - beta_j)
+    a = np.exp(g) * (1 - beta)
+    for t in range(L):
+        St = np.prod(a[:t + 1]) * s0[0]
+        for i in range(t + 1):
+            St = St + np.prod(a[i + 1:t + 1]) * beta[i] * k[i, 0] * v[i]
+        np.testing.assert_allclose(out[t], q[t, 0] * St, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(S[0], St, atol=1e-12, rtol=0)
+
+
+def test_per_step_write_identity():
+    # After token t: S_t^T k_t = (1 - beta ||k||^2) (D_t S_{t-1})^T k_t + beta ||k||^2 v_t,
+    # for any k (not only unit k). Checked step by step on bf16-rounded inputs.
+    import synth
+    c = synth.config(3, B=2, Nk=1, Nv=2, Dk=32, Dv=16, slots=4)
+    q, k, v, beta, g, gk = (c.f64(n) for n in ("q", "k", "v", "beta", "g", "gk"))
+    S = synth.widen(c.state, c.dtype)[c.idx[0], 0]
+    for t in range(c.S):
+        kt, bt = k[0, 0, t], beta[0, 0, t]
+        DS = math.exp(g[0, 0, t]) * np.exp(gk[0, 0, t])[:, None] * S
+        _, S = oracle.sequence(q[0, 0, t:t + 1], k[0, 0, t:t + 1], v[0, 0, t:t + 1],
+                               beta[0, 0, t:t + 1], g=g[0, 0, t:t + 1], gk=gk[0, 0, t:t + 1],
+                               state=S)
+        nk2 = kt @ kt
+        lhs = S.T @ kt
+        rhs = (1 - bt * nk2) * (DS.T @ kt) + bt * nk2 * v[0, 0, t]
+        np.testing.assert_allclose(lhs, rhs, atol=1e-12, rtol=0)
+
+
+def test_contractive_under_decay_and_bounded_beta():
+    # deltanet.rs stability test scenario: 200 random steps, Dk = Dv = 8, norm stays bounded.
+    rng = np.random.default_rng(42)
+    d = 8
+    S = np.zeros((d, d))
+    peak = 0.0
+    for _ in range(200):
+        u = lambda n: rng.uniform(-0.5, 0.5, n)
+        q = _rand_unit(rng, 1, d)
+        k = _rand_unit(rng, 1, d)
+        v = u(d)[None]
+        g = np.array([-math.log1p(math.exp(u(1)[0] * 4))])
+        beta = np.array([1 / (1 + math.exp(-u(1)[0] * 4))])
+        # the decay-and-erase part alone never grows the Frobenius norm
+        _, Sz = oracle.sequence(q, k, np.zeros((1, d)), beta, g=g, state=S)
+        assert np.linalg.norm(Sz) <= np.linalg.norm(S) + 1e-12
+        _, S = oracle.sequence(q, k, v, beta, g=g, state=S)
+        peak = max(peak, np.linalg.norm(S))
+        assert np.isfinite(S).all()
+    assert peak < 20.0
