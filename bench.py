@@ -1,0 +1,334 @@
+"""Benchmark of the Gated Delta Rule library on one MI355X.
+
+Headline: decode tokens/s on the decode step workload (B=64, Nk=16, Nv=32,
+S=1, Dk=Dv=128, bf16, 64-slot pool), with the state traffic as a fraction of
+HBM peak. Secondary entries: speculative decode (B=128, S=4, per-key gate),
+chunked prefill (B=4, S=4096, Nv=32) and, with --varlen, varlen prefill
+without decay (B=16, S<=16384, Nv=64), each with its roofline.
+
+A step is one call of the operator over one batch. Inputs sit in HBM before
+the timed region; decode rotates over enough pool copies that the working set
+exceeds the 256 MB last-level cache. Kernel time comes from HIP events
+recorded on the stream the kernels are launched on. Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gated_deltanet_recurrence_amd as gdr  # noqa: E402
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+METRIC = "decode tok/s + state GB/s (%HBM); prefill tok/s + TFLOP/s (%MFMA), Dk=Dv=128"
+
+
+def dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to("cuda").view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def esize(dtype):
+    return 2 if dtype == "bf16" else 4
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work per call
+# ---------------------------------------------------------------------------
+def decode_bytes(c):
+    """State read once per active sequence and written once per distinct
+    consecutive write slot, plus token inputs, outputs and integers."""
+    e = esize(c.dtype)
+    L = c.valid_lengths()
+    S, slots = c.S, c.state.shape[0]
+    hs = c.Nv * c.Dk * c.Dv * e
+    state = 0
+    tok = 0
+    for b in range(c.B):
+        n = int(L[b]) if c.n_acc is None else int(c.n_acc[b])
+        if L[b] == 0 or n < 1 or n > S or not 0 <= c.idx[b * S + n - 1] < slots:
+            continue
+        writes = 0
+        for t in range(L[b]):
+            w = c.idx[b * S + t]
+            last = t == L[b] - 1 or c.idx[b * S + t + 1] != w
+            writes += int(last and 0 <= w < slots)
+        state += hs * (1 + writes)
+        tok += int(L[b])
+    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * e + (4 * c.Nv if c.g is not None else 0) \
+        + (4 * c.Nv * c.Dk if c.gk is not None else 0)
+    out = c.B * c.S * c.Nv * c.Dv * e
+    ints = c.B * 4 * (2 if c.n_acc is not None else 1) + c.B * c.S * 4
+    return state, state + tok * per_tok + out + ints, tok
+
+
+def prefill_work(c):
+    """(bytes, flops) per call. Flops per token and value head:
+    C(3Dk + 2Dv) + C^2/3 + 6 Dk Dv (triangular products counted at half)."""
+    e = esize(c.dtype)
+    L = c.valid_lengths()
+    T = int(L.sum())
+    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * e + (4 * c.Nv if c.g is not None else 0)
+    out = c.B * c.S * c.Nv * c.Dv * e
+    states = c.B * c.Nv * c.Dk * c.Dv * e * ((1 if c.state is not None else 0) + 1)
+    C = c.chunk
+    f_tok = C * (3 * c.Dk + 2 * c.Dv) + C * C / 3 + 6 * c.Dk * c.Dv
+    return T * per_tok + out + states, T * c.Nv * f_tok, T
+
+
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+def time_calls(calls, steps, warmup, use_graph):
+    """Runs `warmup` then `steps` calls (cycling through `calls`), timed with
+    HIP events on the current stream. Returns (ms per call by events, wall s)."""
+    stream = torch.cuda.current_stream()
+    n = len(calls)
+    if use_graph:
+        for i in range(n):
+            calls[i]()                               # first launch outside capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(n):
+                calls[i]()
+        reps_w = max(1, math.ceil(warmup / n))
+        for _ in range(reps_w):
+            graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(steps / n))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / (reps * n), wall, reps * n
+    for i in range(warmup):
+        calls[i % n]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % n]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall, steps
+
+
+def decode_calls(c, copies):
+    """Pre-marshalled gdr_decode calls, one per copy of the pool and inputs."""
+    lib = gdr.load_library()
+    calls, keep = [], []
+    for _ in range(copies):
+        t = dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), beta=dev(c.beta), g=dev(c.g), gk=dev(c.gk),
+                 pool=dev(c.state), lens=dev(c.lens), idx=dev(c.idx), nacc=dev(c.n_acc))
+        t["out"] = torch.empty((c.B, c.Nv, c.S, c.Dv), dtype=t["q"].dtype, device="cuda")
+        p = lambda x: None if x is None else x.data_ptr()
+        a = gdr.DecodeArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S,
+                           c.Dk, c.Dv, c.state.shape[0], c.idx.size, p(t["q"]), p(t["k"]), p(t["v"]),
+                           p(t["beta"]), p(t["g"]), p(t["gk"]), p(t["pool"]), p(t["lens"]), p(t["idx"]),
+                           p(t["nacc"]), c.scale, p(t["out"]))
+        keep.append((t, a))
+
+        def call(a=a):
+            rc = lib.gdr_decode(a, torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(f"gdr_decode failed: {rc}")
+        calls.append(call)
+    return calls, keep
+
+
+def chunk_calls(c, copies):
+    lib = gdr.load_library()
+    calls, keep = [], []
+    for _ in range(copies):
+        t = dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), beta=dev(c.beta), g=dev(c.g), init=dev(c.state),
+                 lens=dev(c.lens))
+        t["out"] = torch.empty((c.B, c.Nv, c.S, c.Dv), dtype=t["q"].dtype, device="cuda")
+        t["fin"] = torch.empty((c.B, c.Nv, c.Dk, c.Dv), dtype=t["q"].dtype, device="cuda")
+        p = lambda x: None if x is None else x.data_ptr()
+        a = gdr.ChunkArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S, c.Dk,
+                          c.Dv, c.chunk, p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["g"]),
+                          p(t["init"]), p(t["lens"]), c.scale, p(t["out"]), p(t["fin"]))
+        keep.append((t, a))
+
+        def call(a=a):
+            rc = lib.gdr_chunk(a, torch.cuda.current_stream().cuda_stream)
+            if rc:
+                raise RuntimeError(f"gdr_chunk failed: {rc}")
+        calls.append(call)
+    return calls, keep
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline_decode(c, budget_s):
+    import oracle
+    args = (c.f64("q"), c.f64("k"), c.f64("v"), c.f64("beta"),
+            None if c.g is None else c.g.astype(np.float64),
+            None if c.gk is None else c.gk.astype(np.float64), c.lens, c.n_acc, c.idx, c.f64("state"), c.scale)
+    tokens = int(c.valid_lengths().sum())
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(*args)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": tokens * reps / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole decode step workload ({c.B} sequences x {c.Nv} heads), {reps} calls, {el:.1f} s"}
+
+
+def cpu_baseline_prefill(c, units, name):
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    rep = c.Nv // c.Nk
+    L = c.valid_lengths()
+    work = []
+    for b, h in units:
+        kh = h // rep
+        Lb = int(L[b])
+        work.append((synth.widen(c.q[b, kh, :Lb], c.dtype), synth.widen(c.k[b, kh, :Lb], c.dtype),
+                     synth.widen(c.v[b, h, :Lb], c.dtype), synth.widen(c.beta[b, h, :Lb], c.dtype),
+                     None if c.g is None else c.g[b, h, :Lb].astype(np.float64),
+                     None if c.state is None else synth.widen(c.state[b, h], c.dtype)))
+    nt = oracle.num_threads()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(nt) as ex:
+        list(ex.map(lambda w: oracle.sequence(w[0], w[1], w[2], w[3], g=w[4], state=w[5], scale=c.scale), work))
+    el = time.perf_counter() - t0
+    tok = int(sum(L[b] for b, _ in units))
+    return {"value": tok / el, "unit": "token-heads/s", "cores": nt, "kind": "oracle",
+            "sample": f"{len(units)} (sequence, head) units of the {name} workload, {tok} token-heads, {el:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--copies", type=int, default=8, help="decode pool copies rotated per step")
+    ap.add_argument("--varlen", action="store_true", help="also time the varlen prefill workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    torch.cuda.init()
+    gdr.load_library()
+    use_graph = args.launch == "graph"
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
+
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded; distributions of the operator pages' workloads)"}
+    secondary = []
+
+    if args.only in (None, "decode"):
+        log("decode step workload: generating inputs")
+        c = synth.config(2)
+        state_b, bytes_call, tok = decode_bytes(c)
+        calls, keep = decode_calls(c, args.copies)
+        log("decode step workload: timing")
+        ms, wall, nsteps = time_calls(calls, args.steps, args.warmup, use_graph)
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        result.update({
+            "value": tok / (ms * 1e-3), "unit": "tok/s", "ms_per_step": ms,
+            "config": {"workload": "decode step: B=64 Nk=16 Nv=32 S=1 Dk=Dv=128 bf16, 64-slot bf16 pool, "
+                                   "permuted slots, no gk", "global_batch": c.B, "seq_len": c.S,
+                       "parallelism": "none (1 GPU)", "pool_copies_rotated": args.copies,
+                       "launch": args.launch},
+            "state_GBps": state_b / (ms * 1e-3) / 1e9,
+            "state_frac_hbm": state_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "roofline": {"kernel": "decode_kernel<bf16,128,128>", "bound": "hbm", "achieved": gbs,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_launch": bytes_call},
+            "wall_s_timed": wall,
+        })
+        del keep, calls
+        if not args.no_cpu:
+            log("decode step workload: oracle CPU baseline")
+            result["cpu_baseline"] = cpu_baseline_decode(c, 10.0)
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "spec"):
+        log("speculative decode workload")
+        c = synth.config(3)
+        state_b, bytes_call, tok = decode_bytes(c)
+        calls, keep = decode_calls(c, max(2, args.copies // 4))
+        ms, wall, _ = time_calls(calls, args.steps, args.warmup, use_graph)
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        secondary.append({"workload": "speculative decode: B=128 S=4 Nk=16 Nv=32 Dk=Dv=128 bf16, gk, "
+                                      "lengths and accepted counts U{1..4}, 256-slot pool",
+                          "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "state_GBps": state_b / (ms * 1e-3) / 1e9,
+                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                       "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls
+        torch.cuda.empty_cache()
+
+    prefill_sets = []
+    if args.only in (None, "prefill"):
+        prefill_sets.append(("chunked prefill", 4, "B=4 S=4096 Nk=16 Nv=32 Dk=Dv=128 bf16, g, initial state, C=64",
+                             [(0, 0), (1, 9), (2, 18), (3, 27)]))
+    if args.varlen or args.only == "varlen":
+        prefill_sets.append(("varlen prefill", 5, "B=16 S=16384 (lengths U{256..16384}) Nk=16 Nv=64 Dk=Dv=128 "
+                             "bf16, no decay, zero initial state, C=64", [(0, 0), (5, 40)]))
+    for name, cid, desc, units in prefill_sets:
+        log(f"{name}: generating inputs")
+        c = synth.config(cid)
+        bytes_call, flops, tok = prefill_work(c)
+        calls, keep = chunk_calls(c, 2 if cid == 4 else 1)
+        log(f"{name}: timing")
+        steps = max(10, args.steps // 8)
+        ms, wall, _ = time_calls(calls, steps, max(2, args.warmup // 8), use_graph)
+        tf = flops / (ms * 1e-3) / 1e12
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        entry = {"workload": f"{name}: {desc}", "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms,
+                 "tokens_per_call": tok, "TFLOPs": tf, "frac_mfma_bf16": tf / BF16_MFMA_PEAK_TFLOPS,
+                 "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                 "roofline": {"kernel": "chunk_mfma_kernel", "bound": "mfma", "achieved": tf,
+                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                              "traffic": None, "algorithmic_flops_per_launch": flops,
+                              "algorithmic_bytes_per_launch": bytes_call}}
+        del keep, calls
+        torch.cuda.empty_cache()
+        if not args.no_cpu:
+            log(f"{name}: oracle CPU baseline")
+            entry["cpu_baseline"] = cpu_baseline_prefill(c, units, name)
+        secondary.append(entry)
+        del c
+
+    if "value" not in result:
+        # a secondary-only run reports its first entry as the value
+        s0 = secondary[0]
+        result.update({"value": s0["tok_per_s"], "unit": "tok/s", "ms_per_step": s0["ms_per_call"],
+                       "config": {"workload": s0["workload"]}, "roofline": s0["roofline"]})
+    result["secondary"] = secondary
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""Python binding of libgdr.so, the gfx950 Gated Delta Rule library.
+
+Argument marshalling only: every step of both operators runs in the HIP
+kernels behind the C ABI declared in include/gdr.h. PyTorch supplies device
+memory and the current stream. There is no CPU fallback: if the library has
+not been built, importing the binding works but every call raises.
+
+Calls (same names as the C entry points):
+  gdr_decode(...)  recurrent decode over an indexed state pool
+                   (lite_boost.ops.recurrent_gated_delta_rule)
+  gdr_chunk(...)   chunked prefill over padded variable-length inputs
+                   (lite_boost.ops.chunk_gated_delta_rule)
+Errors follow the operator pages: shape problems raise ValueError; dtype,
+device and launch problems raise RuntimeError.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK, GDR_ERR_NULL, GDR_ERR_SHAPE, GDR_ERR_DTYPE, GDR_ERR_UNSUPPORTED, GDR_ERR_LAUNCH = range(6)
+GDR_F32, GDR_BF16 = 0, 1
+
+_vp = ctypes.c_void_p
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Nk", ctypes.c_int32),
+        ("Nv", ctypes.c_int32), ("S", ctypes.c_int32), ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32), ("num_slots", ctypes.c_int32),
+        ("num_state_indices", ctypes.c_int64),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp),
+        ("g", _vp), ("gk", _vp), ("state_pool", _vp),
+        ("actual_seq_lengths", _vp), ("ssm_state_indices", _vp), ("num_accepted_tokens", _vp),
+        ("scale_value", ctypes.c_float), ("out", _vp),
+    ]
+
+
+class ChunkArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("Nk", ctypes.c_int32),
+        ("Nv", ctypes.c_int32), ("S", ctypes.c_int32), ("Dk", ctypes.c_int32),
+        ("Dv", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+        ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("g", _vp),
+        ("initial_state", _vp), ("actual_seq_lengths", _vp),
+        ("scale_value", ctypes.c_float), ("out", _vp), ("final_state", _vp),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Loads libgdr.so and declares its entry points. Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgdr.so is not built ({path}); run gated_deltanet_recurrence_amd/build.py")
+    lib = ctypes.CDLL(path)
+    lib.gdr_decode.restype = ctypes.c_int
+    lib.gdr_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
+    lib.gdr_chunk.restype = ctypes.c_int
+    lib.gdr_chunk.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_status_string.argtypes = [ctypes.c_int]
+    lib.gdr_abi_version.restype = ctypes.c_int32
+    lib.gdr_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc == GDR_OK:
+        return
+    msg = f"{what}: {load_library().gdr_status_string(rc).decode()} (status {rc})"
+    if rc == GDR_ERR_SHAPE:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+_DT = {torch.bfloat16: GDR_BF16, torch.float32: GDR_F32}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype, device, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise RuntimeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise RuntimeError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise RuntimeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices, g=None, gk=None,
+               num_accepted_tokens=None, scale_value=1.0, out=None):
+    """Recurrent decode; updates state_pool in place. Returns (out, state_pool).
+
+    q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); state_pool
+    (slots, Nv, Dk, Dv) — all of one dtype (bfloat16 or float32); g (B, Nv, S)
+    and gk (B, Nv, S, Dk) float32 or None; actual_seq_lengths (B,),
+    ssm_state_indices (B*S,), num_accepted_tokens (B,) or None — int32.
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (B, N, S, D)")
+    B, Nk, S, Dk = k.shape
+    Nv, Dv = v.shape[1], v.shape[3]
+    dt = q.dtype
+    if dt not in _DT:
+        raise RuntimeError(f"unsupported dtype {dt}")
+    dev = q.device
+    if dev.type != "cuda":
+        raise RuntimeError("tensors must be on a GPU")
+    _need(q, "query", dt, dev, (B, Nk, S, Dk))
+    _need(k, "key", dt, dev)
+    _need(v, "value", dt, dev, (B, Nv, S, Dv))
+    _need(beta, "beta", dt, dev, (B, Nv, S))
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (Nv, Dk, Dv):
+        raise ValueError(f"state has shape {tuple(state_pool.shape)}, expected (slots, {Nv}, {Dk}, {Dv})")
+    _need(state_pool, "state", dt, dev)
+    _need(g, "g", torch.float32, dev, (B, Nv, S))
+    _need(gk, "gk", torch.float32, dev, (B, Nv, S, Dk))
+    _need(actual_seq_lengths, "actual_seq_lengths", torch.int32, dev, (B,))
+    _need(ssm_state_indices, "ssm_state_indices", torch.int32, dev)
+    _need(num_accepted_tokens, "num_accepted_tokens", torch.int32, dev, (B,))
+    if out is None:
+        out = torch.empty((B, Nv, S, Dv), dtype=dt, device=dev)
+    _need(out, "out", dt, dev, (B, Nv, S, Dv))
+    a = DecodeArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, state_pool.shape[0], ssm_state_indices.numel(),
+                   _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(gk), _ptr(state_pool),
+                   _ptr(actual_seq_lengths), _ptr(ssm_state_indices), _ptr(num_accepted_tokens),
+                   float(scale_value), _ptr(out))
+    _check(load_library().gdr_decode(ctypes.byref(a), _stream(dev)), "gdr_decode")
+    return out, state_pool
+
+
+def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
+              chunk_size=64, out=None, final_state=None):
+    """Chunked prefill. Returns (out, final_state).
+
+    q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); initial_state
+    (B, Nv, Dk, Dv) or None — one dtype; g (B, Nv, S) float32 or None;
+    actual_seq_lengths (B,) int32 or None. final_state may be initial_state
+    itself (updated in place).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (B, N, S, D)")
+    B, Nk, S, Dk = k.shape
+    Nv, Dv = v.shape[1], v.shape[3]
+    dt = q.dtype
+    if dt not in _DT:
+        raise RuntimeError(f"unsupported dtype {dt}")
+    dev = q.device
+    if dev.type != "cuda":
+        raise RuntimeError("tensors must be on a GPU")
+    _need(q, "query", dt, dev, (B, Nk, S, Dk))
+    _need(k, "key", dt, dev)
+    _need(v, "value", dt, dev, (B, Nv, S, Dv))
+    _need(beta, "beta", dt, dev, (B, Nv, S))
+    _need(initial_state, "initial_state", dt, dev, (B, Nv, Dk, Dv))
+    _need(g, "g", torch.float32, dev, (B, Nv, S))
+    _need(actual_seq_lengths, "actual_seq_lengths", torch.int32, dev, (B,))
+    if out is None:
+        out = torch.empty((B, Nv, S, Dv), dtype=dt, device=dev)
+    if final_state is None:
+        final_state = torch.empty((B, Nv, Dk, Dv), dtype=dt, device=dev)
+    _need(out, "out", dt, dev, (B, Nv, S, Dv))
+    _need(final_state, "final_state", dt, dev, (B, Nv, Dk, Dv))
+    a = ChunkArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, int(chunk_size),
+                  _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
+                  _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state))
+    _check(load_library().gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")
+    return out, final_state

@@ -1,0 +1,93 @@
+// C ABI of libgdr.so: argument validation on the host, kernel selection and
+// launch on the caller's stream. The operations and argument contracts are
+// documented in include/gdr.h.
+#include "gdr.h"
+#include "gdr_common.h"
+
+namespace {
+
+bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+gdr_status from_launch(hipError_t e, bool supported)
+{
+    if (!supported) return GDR_ERR_UNSUPPORTED;
+    return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char *gdr_status_string(gdr_status s)
+{
+    switch (s) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_NULL: return "a required pointer is NULL";
+    case GDR_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case GDR_ERR_DTYPE: return "unknown element type";
+    case GDR_ERR_UNSUPPORTED: return "no kernel for these head sizes, chunk size or alignment";
+    case GDR_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
+{
+    if (!a) return GDR_ERR_NULL;
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
+    if (a->B < 0 || a->S < 1 || a->S > 8 || a->Nk < 1 || a->Nv < 1 || a->Dk < 1 || a->Dv < 1 ||
+        a->num_slots < 1 || a->Nv % a->Nk != 0)
+        return GDR_ERR_SHAPE;
+    if (a->num_state_indices != (int64_t)a->B * a->S) return GDR_ERR_SHAPE;
+    if (a->B == 0) return GDR_OK;
+    if (!a->q || !a->k || !a->v || !a->beta || !a->state_pool || !a->out || !a->actual_seq_lengths ||
+        !a->ssm_state_indices)
+        return GDR_ERR_NULL;
+    if ((int64_t)a->B * a->Nv * 2 > 0x7fffffffLL) return GDR_ERR_UNSUPPORTED;
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->state_pool) ||
+        !aligned16(a->out) || !aligned16(a->gk))
+        return GDR_ERR_UNSUPPORTED;
+
+    gdr::DecodeParams p;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta;
+    p.g = a->g; p.gk = a->gk;
+    p.pool = a->state_pool;
+    p.lens = a->actual_seq_lengths; p.idx = a->ssm_state_indices; p.nacc = a->num_accepted_tokens;
+    p.out = a->out;
+    p.scale = a->scale_value;
+    p.B = a->B; p.Nk = a->Nk; p.Nv = a->Nv; p.S = a->S; p.slots = a->num_slots;
+    bool ok = false;
+    hipError_t e = gdr::launch_decode(a->dtype, a->Dk, a->Dv, p, (hipStream_t)stream, &ok);
+    return from_launch(e, ok);
+}
+
+gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
+{
+    if (!a) return GDR_ERR_NULL;
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
+    if (a->B < 0 || a->S < 0 || a->Nk < 1 || a->Nv < 1 || a->Dk < 1 || a->Dv < 1 ||
+        a->chunk_size < 1 || a->Nv % a->Nk != 0)
+        return GDR_ERR_SHAPE;
+    if (a->B == 0) return GDR_OK;
+    if (!a->q || !a->k || !a->v || !a->beta || !a->out || !a->final_state) return GDR_ERR_NULL;
+    if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) ||
+        !aligned16(a->initial_state) || !aligned16(a->final_state))
+        return GDR_ERR_UNSUPPORTED;
+
+    gdr::ChunkParams p;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta;
+    p.g = a->g;
+    p.init = a->initial_state;
+    p.lens = a->actual_seq_lengths;
+    p.out = a->out;
+    p.fin = a->final_state;
+    p.scale = a->scale_value;
+    p.B = a->B; p.Nk = a->Nk; p.Nv = a->Nv; p.S = a->S;
+    bool ok = false;
+    hipError_t e = gdr::launch_chunk(a->dtype, a->Dk, a->Dv, a->chunk_size, p, (hipStream_t)stream, &ok);
+    return from_launch(e, ok);
+}
+
+}  // extern "C"

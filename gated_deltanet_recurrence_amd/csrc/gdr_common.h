@@ -1,0 +1,148 @@
+// Internal declarations shared by the host entry points and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// Kernel-side view of a decode call (all device pointers; sizes validated on the host).
+struct DecodeParams {
+    const void *q, *k, *v, *beta;
+    const float *g, *gk;
+    void *pool;
+    const int32_t *lens, *idx, *nacc;
+    void *out;
+    float scale;
+    int32_t B, Nk, Nv, S, slots;
+};
+
+// Kernel-side view of a chunked prefill call.
+struct ChunkParams {
+    const void *q, *k, *v, *beta;
+    const float *g;
+    const void *init;
+    const int32_t *lens;
+    void *out;
+    void *fin;
+    float scale;
+    int32_t B, Nk, Nv, S;
+};
+
+// Launchers: return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
+hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported);
+hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, hipStream_t s, bool *supported);
+
+// ---------------------------------------------------------------------------
+// Element access helpers (device). bf16 values travel as raw 16-bit patterns;
+// widening is exact (shift into the high half of a float), narrowing rounds to
+// nearest even through the hardware converter.
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    __bf16 x = (__bf16)a;
+    __bf16 y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
+{
+    __bf16 y = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, y);
+}
+
+// Loads N consecutive elements (N * sizeof(T) in {4, 8, 16} bytes, aligned) as floats.
+template <typename T, int N> struct VecIO;
+
+template <> struct VecIO<float, 4> {
+    static __device__ __forceinline__ void load(const float *p, float *o)
+    {
+        float4 v = *reinterpret_cast<const float4 *>(p);
+        o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    }
+    static __device__ __forceinline__ void store(float *p, const float *o)
+    {
+        *reinterpret_cast<float4 *>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+};
+template <> struct VecIO<float, 2> {
+    static __device__ __forceinline__ void load(const float *p, float *o)
+    {
+        float2 v = *reinterpret_cast<const float2 *>(p);
+        o[0] = v.x; o[1] = v.y;
+    }
+    static __device__ __forceinline__ void store(float *p, const float *o)
+    {
+        *reinterpret_cast<float2 *>(p) = make_float2(o[0], o[1]);
+    }
+};
+template <> struct VecIO<float, 1> {
+    static __device__ __forceinline__ void load(const float *p, float *o) { o[0] = *p; }
+    static __device__ __forceinline__ void store(float *p, const float *o) { *p = o[0]; }
+};
+template <> struct VecIO<bf16_t, 8> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float *o)
+    {
+        uint4 v = *reinterpret_cast<const uint4 *>(p);
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, const float *o)
+    {
+        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+    }
+};
+template <> struct VecIO<bf16_t, 4> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float *o)
+    {
+        uint2 v = *reinterpret_cast<const uint2 *>(p);
+        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, const float *o)
+    {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+    }
+};
+template <> struct VecIO<bf16_t, 2> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float *o)
+    {
+        uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+        o[0] = bf16_lo(v); o[1] = bf16_hi(v);
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, const float *o)
+    {
+        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(o[0], o[1]);
+    }
+};
+
+template <> struct VecIO<bf16_t, 1> {
+    static __device__ __forceinline__ void load(const bf16_t *p, float *o) { o[0] = to_f32(*p); }
+    static __device__ __forceinline__ void store(bf16_t *p, const float *o) { *p = from_f32<bf16_t>(o[0]); }
+};
+
+// Loads N consecutive elements with the widest aligned vector loads that fit
+// (N is a power of two; the address is aligned to min(N, 16 / sizeof(T)) elements).
+template <typename T, int N>
+__device__ __forceinline__ void load_run(const T *p, float *o)
+{
+    constexpr int W0 = 16 / (int)sizeof(T);
+    constexpr int W = N < W0 ? N : W0;
+#pragma unroll
+    for (int i = 0; i < N; i += W) VecIO<T, W>::load(p + i, o + i);
+}
+
+// Wave-uniform value in a scalar register.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+}  // namespace gdr

@@ -1,0 +1,176 @@
+/*
+ * gdr.h — C ABI of the MI355X (gfx950) Gated Delta Rule library, libgdr.so.
+ *
+ * The Gated Delta Rule, per token t and per value head, on a state
+ * S in R^{Dk x Dv} (rows: key dimension, columns: value dimension):
+ *
+ *   S     <- S * exp(g_t)           (decode: row i also scaled by exp(gk_t[i]))
+ *   kv    <- S^T k_t                memory read
+ *   S     <- S + k_t (beta_t (v_t - kv))^T
+ *   o_t   <- scale * S^T q_t
+ *
+ * (lite_boost.ops.recurrent_gated_delta_rule, MindSpore Lite API page:
+ * algorithm section; lite_boost.ops.chunk_gated_delta_rule: formula section;
+ * the Gated DeltaNet blog post, torch_recurrent_gated_delta_rule: the decay is
+ * applied before the memory read and the write is the outer product k delta^T.)
+ *
+ * Conventions shared by both calls
+ *  - Every tensor pointer is a DEVICE pointer to a dense, row-major
+ *    (C-contiguous) buffer in the layout given below; the caller owns every
+ *    buffer. The library allocates nothing, keeps no state between calls and
+ *    never synchronises the stream; calls are thread-safe.
+ *  - The work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
+ *    stream). Device integers are never read by the host.
+ *  - Element type `dtype` applies to q, k, v, beta, the states and out:
+ *    GDR_BF16 (bfloat16, stored rounded to nearest even) or GDR_F32.
+ *    g and gk are always float32. Integers are int32.
+ *  - Value head h uses key/query head h / (Nv / Nk): the repeat-interleave
+ *    grouping of the blog post's layer code. Nv must be a multiple of Nk.
+ *  - Return codes are produced on the host before anything is enqueued
+ *    (except GDR_ERR_LAUNCH, from the launch itself). No value of g or gk is
+ *    checked (the operator pages leave their sign unchecked on purpose).
+ *  - Inputs and outputs must not overlap, except where stated.
+ *  - q, k, v, the states, out and gk must be 16-byte aligned
+ *    (GDR_ERR_UNSUPPORTED otherwise); torch allocations always are.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stdint.h>
+
+/* Symbols of the shared library; everything else in it is hidden. */
+#if defined(__GNUC__)
+#define GDR_API __attribute__((visibility("default")))
+#else
+#define GDR_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    GDR_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes (ValueError) */
+    GDR_ERR_DTYPE = 3,       /* unknown dtype code                              */
+    GDR_ERR_UNSUPPORTED = 4, /* head sizes / chunk size with no compiled kernel */
+    GDR_ERR_LAUNCH = 5       /* the kernel launch failed (RuntimeError)         */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/*
+ * Recurrent decode over an indexed state pool.
+ * (lite_boost.ops.recurrent_gated_delta_rule: signature, parameters, returns,
+ * errors and notes — decode only, S <= 8, grouped heads.)
+ *
+ * Sizes: B >= 0 sequences, 1 <= S <= 8 token positions per sequence,
+ *        Nk, Nv heads, head sizes Dk, Dv, num_slots >= 1 pool slots.
+ * Tensors (device, row-major):
+ *   q, k      (B, Nk, S, Dk)   dtype; callers pass L2-normalised vectors
+ *   v         (B, Nv, S, Dv)   dtype
+ *   beta      (B, Nv, S)       dtype, write strength in [0, 1]
+ *   g         (B, Nv, S)       float32 log decay; NULL means alpha = 1
+ *   gk        (B, Nv, S, Dk)   float32 per-key log decay, or NULL
+ *   state_pool (num_slots, Nv, Dk, Dv) dtype — read and UPDATED IN PLACE
+ *   actual_seq_lengths (B)     int32; L_b = clamp(value, 0, S)
+ *   num_accepted_tokens (B)    int32, or NULL meaning equal to L_b
+ *   ssm_state_indices (num_state_indices) int32, one slot per token
+ *                              position; num_state_indices must equal B*S
+ *   out       (B, Nv, S, Dv)   dtype
+ *   scale_value                multiplies every output (1/sqrt(Dk) is usual)
+ * Semantics per sequence b (n_b = num_accepted_tokens[b] or L_b):
+ *   the entering state is read from slot ssm_state_indices[b*S + n_b - 1];
+ *   tokens t = 0..L_b-1 are applied in order, carrying the state in float32;
+ *   after token t the state is stored (rounded to dtype) into slot
+ *   ssm_state_indices[b*S + t] (a store that token t+1 would overwrite in
+ *   the same slot may be skipped); out[b, :, t] = 0 for t >= L_b.
+ *   If L_b == 0, n_b is outside [1, S] or the read slot is outside
+ *   [0, num_slots), the sequence writes zeros to out and touches no slot;
+ *   a write slot outside [0, num_slots) skips that store only.
+ *   Two sequences of one call must not share a slot (the result is undefined).
+ *   A call is not idempotent: it advances the pool.
+ * Supported: Dk, Dv in {16, 32, 64, 128}; both dtypes.
+ * Errors: GDR_ERR_NULL if a is NULL or q, k, v, beta, state_pool, out,
+ *   actual_seq_lengths or ssm_state_indices is NULL (when B > 0);
+ *   GDR_ERR_SHAPE if B < 0, S outside [1, 8], Nk, Nv, Dk, Dv or num_slots
+ *   < 1, Nv % Nk != 0, or num_state_indices != B*S; GDR_ERR_DTYPE;
+ *   GDR_ERR_UNSUPPORTED; GDR_ERR_LAUNCH. B == 0 is a no-op.
+ */
+typedef struct {
+    int32_t dtype;
+    int32_t B, Nk, Nv, S, Dk, Dv;
+    int32_t num_slots;
+    int64_t num_state_indices;
+    const void *q, *k, *v, *beta;
+    const float *g, *gk;
+    void *state_pool;
+    const int32_t *actual_seq_lengths;
+    const int32_t *ssm_state_indices;
+    const int32_t *num_accepted_tokens;
+    float scale_value;
+    void *out;
+} gdr_decode_args;
+
+GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
+
+/*
+ * Chunked prefill over padded, variable-length BNSD inputs.
+ * (lite_boost.ops.chunk_gated_delta_rule: signature, parameters, formula,
+ * returns; the blog post's torch_chunk_gated_delta_rule: right-padding to a
+ * multiple of the chunk, in-chunk cumulative decay, the triangular solve, and
+ * the pass over chunks that carries the state.)
+ *
+ * Sizes: B >= 0, S >= 0 (padded length), Nk, Nv, Dk, Dv, chunk_size.
+ * Tensors (device, row-major):
+ *   q, k      (B, Nk, S, Dk)   dtype
+ *   v         (B, Nv, S, Dv)   dtype
+ *   beta      (B, Nv, S)       dtype
+ *   g         (B, Nv, S)       float32 log decay, or NULL meaning alpha = 1
+ *   initial_state (B, Nv, Dk, Dv) dtype, or NULL meaning zeros
+ *   actual_seq_lengths (B)     int32 or NULL (all S); L_b = clamp(value, 0, S)
+ *   out       (B, Nv, S, Dv)   dtype; rows t >= L_b are written as exact zeros
+ *   final_state (B, Nv, Dk, Dv) dtype: the state after token L_b - 1 (the
+ *                              initial state when L_b == 0). final_state MAY
+ *                              alias initial_state (same pointer).
+ *   scale_value                multiplies every output
+ * Inputs at positions t >= L_b are never read.
+ * The result equals the token-by-token recurrence up to rounding; the state
+ * is carried in float32 between chunks.
+ * Supported: bf16 with Dk = Dv = 128 and chunk_size 64 (matrix-core path);
+ *   f32 with Dk = Dv in {16, 32} and chunk_size in {16, 32, 64}, or
+ *   Dk = Dv = 64 and chunk_size in {16, 32}.
+ * Errors: GDR_ERR_NULL if a, q, k, v, beta, out or final_state is NULL
+ *   (when B > 0); GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1,
+ *   Nv % Nk != 0 or chunk_size < 1; GDR_ERR_DTYPE; GDR_ERR_UNSUPPORTED;
+ *   GDR_ERR_LAUNCH. B == 0 is a no-op.
+ */
+typedef struct {
+    int32_t dtype;
+    int32_t B, Nk, Nv, S, Dk, Dv;
+    int32_t chunk_size;
+    const void *q, *k, *v, *beta;
+    const float *g;
+    const void *initial_state;
+    const int32_t *actual_seq_lengths;
+    float scale_value;
+    void *out;
+    void *final_state;
+} gdr_chunk_args;
+
+GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+GDR_API const char *gdr_status_string(gdr_status s);
+
+/* ABI version of this header (incremented on any layout change). */
+GDR_API int32_t gdr_abi_version(void);
+
+#define GDR_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

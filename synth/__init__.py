@@ -8,6 +8,7 @@ apply upstream of the operators, and bf16 storage rounding.
 Input recipes (Gated DeltaNet blog post, gate computation; inferencelayer
 deltanet.rs, module header and l2norm):
   q, k  : standard normal per head vector, then x / sqrt(sum(x^2) + 1e-6)
+          (in float32)
   v     : standard normal
   beta  : sigmoid(N(0, 1))                      write strength in (0, 1)
   g     : -exp(A_log[h]) * softplus(a + dt_bias[h]) with A_log ~ U(-2, 1),
@@ -34,9 +35,13 @@ BF16_NAN = np.uint16(0x7FC0)
 def bf16_bits(x) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest even (NaN -> quiet NaN)."""
     x32 = np.ascontiguousarray(x, dtype=np.float32)
-    u = x32.view(np.uint32).astype(np.uint64)
-    r = ((u >> 16) & 1) + 0x7FFF
-    out = ((u + r) >> 16).astype(np.uint16)
+    u = x32.view(np.uint32)
+    # u + bias can wrap only for NaN bit patterns, which are replaced below
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    out = r.astype(np.uint16)
     nan = np.isnan(x32)
     if nan.any():
         out[nan] = BF16_NAN
@@ -54,8 +59,10 @@ def _rng(base, tid, b=None):
 
 
 def _l2n(x):
-    x = x.astype(np.float64)
-    return x / np.sqrt((x * x).sum(-1, keepdims=True) + 1e-6)
+    """x / sqrt(sum(x^2) + 1e-6) over the last axis, in place, float32."""
+    n = np.sqrt(np.einsum("...d,...d->...", x, x)[..., None] + np.float32(1e-6))
+    x /= n
+    return x
 
 
 def _softplus(x):
@@ -121,15 +128,22 @@ class Case:
 
 
 def _per_b(base, tid, B, fn, threads=8):
-    """Runs fn(rng, b) for every batch slice (independent streams) and stacks."""
+    """Runs fn(rng, b) for every batch slice (independent streams) into one array."""
+    first = fn(_rng(base, tid, 0), 0)
+    out = np.empty((B,) + first.shape, dtype=first.dtype)
+    out[0] = first
+    del first
+
     def one(b):
-        return fn(_rng(base, tid, b), b)
-    if B <= 1 or threads <= 1:
-        parts = [one(b) for b in range(B)]
-    else:
-        with ThreadPoolExecutor(min(threads, B)) as ex:
-            parts = list(ex.map(one, range(B)))
-    return np.stack(parts)
+        out[b] = fn(_rng(base, tid, b), b)
+    if B > 1:
+        if threads <= 1:
+            for b in range(1, B):
+                one(b)
+        else:
+            with ThreadPoolExecutor(min(threads, B - 1)) as ex:
+                list(ex.map(one, range(1, B)))
+    return out
 
 
 def _unit_vectors(base, tid, B, N, S, D, dtype):
@@ -142,7 +156,7 @@ def _normals(base, tid, B, shape, dtype, std=1.0):
     def fn(rng, b):
         x = rng.standard_normal(shape, dtype=np.float32)
         if std != 1.0:
-            x = x * np.float32(std)
+            x *= np.float32(std)
         return _store(x, dtype)
     return _per_b(base, tid, B, fn)
 

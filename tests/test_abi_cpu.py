@@ -1,0 +1,149 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, its argument structs match the header byte for byte, and every
+validation error is returned before anything touches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_recurrence_amd as gdr
+from gated_deltanet_recurrence_amd import build as gbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gbuild.LIB):
+        gbuild.build()
+    return gdr.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = re.findall(r"GDR_API\s+[\w\s\*]+?\b(gdr_\w+)\s*\(", open(HEADER).read())
+    assert set(names) == {"gdr_decode", "gdr_chunk", "gdr_status_string", "gdr_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", gbuild.LIB], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert exported == set(names)
+
+
+def test_abi_version_and_status_strings(lib):
+    m = re.search(r"#define GDR_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.gdr_abi_version() == int(m.group(1))
+    for code in range(6):
+        assert lib.gdr_status_string(code)
+    assert lib.gdr_status_string(99) == b"unknown status"
+
+
+def _c_layout(tmp_path, struct, fields):
+    src = tmp_path / "layout.c"
+    body = "".join(f'printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields)
+    src.write_text(f'#include <stdio.h>\n#include <stddef.h>\n#include "gdr.h"\n'
+                   f'int main(void){{printf("sizeof %zu\\n", sizeof({struct}));{body}return 0;}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    return dict((l.split()[0], int(l.split()[1])) for l in lines if l)
+
+
+@pytest.mark.parametrize("struct,cls", [("gdr_decode_args", gdr.DecodeArgs), ("gdr_chunk_args", gdr.ChunkArgs)])
+def test_ctypes_structs_match_header(tmp_path, struct, cls):
+    fields = [f for f, _ in cls._fields_]
+    c = _c_layout(tmp_path, struct, fields)
+    assert c["sizeof"] == ctypes.sizeof(cls)
+    for f in fields:
+        assert c[f] == getattr(cls, f).offset, f
+
+
+FAKE = 0x100000   # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _dec(**kw):
+    a = dict(dtype=gdr.GDR_BF16, B=2, Nk=2, Nv=4, S=1, Dk=128, Dv=128, num_slots=4,
+             num_state_indices=2, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, gk=None,
+             state_pool=FAKE, actual_seq_lengths=FAKE, ssm_state_indices=FAKE,
+             num_accepted_tokens=None, scale_value=1.0, out=FAKE)
+    a.update(kw)
+    return gdr.DecodeArgs(**a)
+
+
+def _chk(**kw):
+    a = dict(dtype=gdr.GDR_BF16, B=2, Nk=2, Nv=4, S=100, Dk=128, Dv=128, chunk_size=64,
+             q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, initial_state=None,
+             actual_seq_lengths=None, scale_value=1.0, out=FAKE, final_state=FAKE)
+    a.update(kw)
+    return gdr.ChunkArgs(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), gdr.GDR_ERR_DTYPE),
+    (dict(S=0), gdr.GDR_ERR_SHAPE),
+    (dict(S=9, num_state_indices=18), gdr.GDR_ERR_SHAPE),
+    (dict(Nv=3), gdr.GDR_ERR_SHAPE),
+    (dict(B=-1), gdr.GDR_ERR_SHAPE),
+    (dict(num_slots=0), gdr.GDR_ERR_SHAPE),
+    (dict(num_state_indices=3), gdr.GDR_ERR_SHAPE),
+    (dict(Dk=0), gdr.GDR_ERR_SHAPE),
+    (dict(q=None), gdr.GDR_ERR_NULL),
+    (dict(state_pool=None), gdr.GDR_ERR_NULL),
+    (dict(ssm_state_indices=None), gdr.GDR_ERR_NULL),
+    (dict(actual_seq_lengths=None), gdr.GDR_ERR_NULL),
+    (dict(out=None), gdr.GDR_ERR_NULL),
+    (dict(Dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(Dv=256), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(v=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(gk=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(B=0, num_state_indices=0, q=None, out=None), gdr.GDR_OK),
+])
+def test_decode_validation(lib, kw, code):
+    a = _dec(**kw)
+    assert lib.gdr_decode(ctypes.byref(a), None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=-1), gdr.GDR_ERR_DTYPE),
+    (dict(S=-1), gdr.GDR_ERR_SHAPE),
+    (dict(Nv=5), gdr.GDR_ERR_SHAPE),
+    (dict(chunk_size=0), gdr.GDR_ERR_SHAPE),
+    (dict(Nk=0), gdr.GDR_ERR_SHAPE),
+    (dict(k=None), gdr.GDR_ERR_NULL),
+    (dict(final_state=None), gdr.GDR_ERR_NULL),
+    (dict(Dk=64, Dv=64), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(chunk_size=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dtype=gdr.GDR_F32, Dk=128, Dv=128), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dtype=gdr.GDR_F32, Dk=64, Dv=64, chunk_size=64), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(B=0, q=None, out=None), gdr.GDR_OK),
+])
+def test_chunk_validation(lib, kw, code):
+    a = _chk(**kw)
+    assert lib.gdr_chunk(ctypes.byref(a), None) == code
+
+
+def test_null_args_struct(lib):
+    assert lib.gdr_decode(None, None) == gdr.GDR_ERR_NULL
+    assert lib.gdr_chunk(None, None) == gdr.GDR_ERR_NULL
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    x = torch.zeros(1, 1, 1, 16)
+    with pytest.raises(RuntimeError):
+        gdr.gdr_chunk(x, x, x, torch.zeros(1, 1, 1))
+    with pytest.raises(RuntimeError):
+        gdr.gdr_decode(x, x, x, torch.zeros(1, 1, 1), torch.zeros(1, 1, 16, 16),
+                       torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32))
+
+
+def test_binding_maps_status_to_exceptions(lib):
+    with pytest.raises(ValueError):
+        gdr._check(gdr.GDR_ERR_SHAPE, "x")
+    for code in (gdr.GDR_ERR_NULL, gdr.GDR_ERR_DTYPE, gdr.GDR_ERR_UNSUPPORTED, gdr.GDR_ERR_LAUNCH):
+        with pytest.raises(RuntimeError):
+            gdr._check(code, "x")
+    gdr._check(gdr.GDR_OK, "x")
