@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--varlen", action="store_true", help="also time the varlen prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen"], default=None)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -238,6 +240,14 @@ def main():
     torch.cuda.init()
     gdr.load_library()
     use_graph = args.launch == "graph"
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)
 
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -142,6 +142,16 @@ __device__ __forceinline__ void load_run(const T *p, float *o)
     for (int i = 0; i < N; i += W) VecIO<T, W>::load(p + i, o + i);
 }
 
+// Read-only int32 input that no kernel writes during a call (lengths, slot
+// indices, accepted counts): read through the constant address space so a
+// wave-uniform index becomes a scalar load, which does not queue behind the
+// wave's outstanding vector loads and stores.
+typedef const __attribute__((address_space(4))) int32_t *cint_ptr;
+__device__ __forceinline__ int32_t ld_const(const int32_t *p, size_t i)
+{
+    return ((cint_ptr)p)[i];
+}
+
 // Wave-uniform value in a scalar register.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

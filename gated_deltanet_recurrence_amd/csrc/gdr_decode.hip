@@ -11,18 +11,51 @@
 // written once per call), so each wavefront owns one column tile of one
 // (b, h) state and keeps it in registers, in float32, across all tokens of
 // the call. The tile is TV columns wide: each lane holds VEC consecutive
-// columns (one 16-byte load for bf16 and TV = 64) of RPL consecutive rows. The
-// two reductions over the key dimension (S^T k and S^T q) are a per-lane sum
-// over its rows followed by a butterfly over the lanes that share the same
-// columns. The columns of S evolve independently, so tiles need no exchange.
-// Per call and head the state is read once and written once per distinct
-// consecutive write slot; q/k/v/beta/g/gk/out are the only other traffic.
+// columns (one 16-byte load for bf16) of RPL consecutive rows. The lanes that
+// share a column group sit next to each other (row group = low lane bits), so
+// the two reductions over the key dimension (S^T k and S^T q) are a per-lane
+// sum over its rows followed by an all-reduce inside a 16-lane DPP row
+// (rotations by 8, 4, 2, 1), with no trip through the LDS crossbar. The
+// columns of S evolve independently, so tiles need no exchange. Per call and
+// head the state is read once and written once per distinct consecutive write
+// slot; q/k/v/beta/g/gk/out are the only other traffic.
 #include "gdr_common.h"
 
 namespace gdr {
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over each aligned group of G consecutive lanes; every lane of the group
+// receives the total. G <= 16 stays inside one DPP row.
+template <int G>
+__device__ __forceinline__ float group_sum(float x)
+{
+    if constexpr (G >= 16) {
+        x += dpp<0x128>(x);   // row_ror:8
+        x += dpp<0x124>(x);   // row_ror:4
+        x += dpp<0x122>(x);   // row_ror:2
+        x += dpp<0x121>(x);   // row_ror:1
+        if constexpr (G >= 32) x += __shfl_xor(x, 16);
+        if constexpr (G >= 64) x += __shfl_xor(x, 32);
+    } else if constexpr (G == 8) {
+        x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+        x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+        x += dpp<0x141>(x);   // row_half_mirror
+    } else if constexpr (G == 4) {
+        x += dpp<0xB1>(x);
+        x += dpp<0x4E>(x);
+    } else if constexpr (G == 2) {
+        x += dpp<0xB1>(x);
+    }
+    return x;
+}
+
 template <typename T, int DK, int DV, int TV, int VEC>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
+__global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
 {
     static_assert(DV % TV == 0 && TV % VEC == 0, "tile shape");
     constexpr int CG = TV / VEC;   // lanes across the tile's columns
@@ -41,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
     const int b = wave / (NT * Nv);
     const int kh = h / (Nv / p.Nk);
 
-    const int cg = lane % CG, rg = lane / CG;
+    const int rg = lane % RG, cg = lane / RG;
     const int col = tile * TV + cg * VEC;
     const int row0 = rg * RPL;
 
@@ -56,11 +89,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
     const size_t qkh = (size_t)b * p.Nk + kh;              // (b, kh) row of q / k
 
     // Integer resolution: lengths clamped, accepted count, read slot.
-    int L = p.lens[b];
+    int L = ld_const(p.lens, b);
     L = L < 0 ? 0 : (L > S ? S : L);
-    const int n = p.nacc ? p.nacc[b] : L;
+    const int n = p.nacc ? ld_const(p.nacc, b) : L;
     int r = -1;
-    if (L > 0 && n >= 1 && n <= S) r = p.idx[(size_t)b * S + n - 1];
+    if (L > 0 && n >= 1 && n <= S) r = ld_const(p.idx, (size_t)b * S + n - 1);
     const bool active = r >= 0 && r < p.slots;
 
     float zero[VEC];
@@ -116,9 +149,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
             kv[c] = s;
         }
 #pragma unroll
-        for (int m = CG; m < 64; m <<= 1)
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) kv[c] += __shfl_xor(kv[c], m);
+        for (int c = 0; c < VEC; ++c) kv[c] = group_sum<RG>(kv[c]);
 
         // Delta write S += k (beta (v - kv))^T, and the output S^T q.
         float o[VEC];
@@ -134,9 +165,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
             o[c] = s;
         }
 #pragma unroll
-        for (int m = CG; m < 64; m <<= 1)
-#pragma unroll
-            for (int c = 0; c < VEC; ++c) o[c] += __shfl_xor(o[c], m);
+        for (int c = 0; c < VEC; ++c) o[c] = group_sum<RG>(o[c]);
         if (rg == 0) {
 #pragma unroll
             for (int c = 0; c < VEC; ++c) o[c] *= p.scale;
@@ -145,8 +174,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
 
         // Store the state into this token's slot unless the next token
         // overwrites the same slot.
-        const int w = p.idx[(size_t)b * S + t];
-        const bool last = (t == L - 1) || (p.idx[(size_t)b * S + t + 1] != w);
+        const int w = ld_const(p.idx, (size_t)b * S + t);
+        const bool last = (t == L - 1) || (ld_const(p.idx, (size_t)b * S + t + 1) != w);
         if (last && w >= 0 && w < p.slots) {
             T *sp = pool + ((size_t)w * Nv + h) * DK * DV + (size_t)row0 * DV + col;
 #pragma unroll
@@ -158,14 +187,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p)
 }
 
 // Tile and vector width per (type, Dk, Dv): 16-byte row segments where the
-// tile holds enough elements, a 64-column (128-byte bf16) tile at most.
-#ifndef GDR_DECODE_TV_MAX
-#define GDR_DECODE_TV_MAX 32
-#endif
+// tile holds enough elements, a 32-column tile at most (measured fastest on
+// MI355X among 16/32/64-column tiles and 1-8 waves per workgroup).
 template <typename T, int DK, int DV>
 static hipError_t launch_one(const DecodeParams &p, hipStream_t s)
 {
-    constexpr int TV_MAX = GDR_DECODE_TV_MAX;
+    constexpr int TV_MAX = 32;
     constexpr int TV = DV > TV_MAX ? TV_MAX : DV;
     constexpr int VMAX = 16 / (int)sizeof(T);
     constexpr int PER_LANE = DK * TV / 64;
@@ -173,7 +200,7 @@ static hipError_t launch_one(const DecodeParams &p, hipStream_t s)
     constexpr int VEC = VEC0 > TV ? TV : VEC0;
     constexpr int NT = DV / TV;
     const long long waves = (long long)p.B * p.Nv * NT;
-    const int wpb = 4;
+    const int wpb = 2;
     const dim3 grid((unsigned)((waves + wpb - 1) / wpb)), block(64 * wpb);
     DecodeParams pc = p;
     void *args[] = {&pc};
