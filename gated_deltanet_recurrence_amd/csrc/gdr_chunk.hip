@@ -9,9 +9,8 @@
 //
 //   A[r,i] = beta_r (k_r . k_i) exp(gamma_r - gamma_i)       i <  r   (else 0)
 //   P[r,i] =        (q_r . k_i) exp(gamma_r - gamma_i)       i <= r   (else 0)
-//   T      = (I + A)^-1                                      unit lower triangular
 //   X      = diag(beta) (V - diag(exp(gamma)) K S0)
-//   Vnew   = T X                                            what each token writes
+//   Vnew   = (I + A)^-1 X                                   what each token writes
 //   O      = scale (diag(exp(gamma)) Q S0 + P Vnew)
 //   S      = exp(gamma_last) S0 + (diag(exp(gamma_last - gamma)) K)^T Vnew
 //
@@ -22,18 +21,16 @@
 //
 // Two kernels:
 //  * chunk_mfma_kernel — bf16 I/O, Dk = Dv = 128, C = 64. One workgroup of
-//    four wavefronts per (sequence, value head, 64-column tile of Dv); the
+//    eight wavefronts per (sequence, value head, 64-column tile of Dv); the
 //    columns of S evolve independently, so each tile carries its own slice of
 //    the state through all chunks in float32 MFMA accumulators. All dense
 //    products run on v_mfma_f32_16x16x32_bf16 with bf16 operands staged in LDS
-//    in the layout each operand needs (16-byte reads). T is built per chunk:
-//    each 16x16 diagonal block as the finite product
-//    (I - A)(I + A^2)(I + A^4)(I + A^8) (A is nilpotent of index 16), computed
-//    in registers with v_mfma_f32_16x16x16_bf16 (a result's register layout
-//    is directly the right-hand operand layout, and its transpose the
-//    left-hand one), then the off-diagonal blocks by block forward
-//    substitution, T_ij = -T_ii sum_{j<=m<i} A_im T_mj, one block diagonal at
-//    a time.
+//    in the layout each operand needs (16-byte reads). T is never formed:
+//    each 16x16 diagonal block of (I + A) is inverted as the finite product
+//    (I - A)(I + A^2)(I + A^4)(I + A^8) (A is nilpotent of index 16) in
+//    registers with v_mfma_f32_16x16x16_bf16 (a result's register layout is
+//    directly the right-hand operand layout, and its transpose the left-hand
+//    one), and (I + A) Vnew = X is solved by block forward substitution.
 //  * chunk_f32_kernel — float32 I/O, small heads. The same chunk algorithm in
 //    plain float32 arithmetic; T by row-wise forward substitution.
 #include <atomic>
@@ -45,6 +42,7 @@ namespace gdr {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
 {
@@ -78,24 +76,38 @@ constexpr int NT = DV / DVT; // column tiles per head
 constexpr int LDK = DK + 8;  // padded row stride (elements) of 128-wide bf16 rows
 constexpr int LDC = C + 8;   // padded row stride of 64-wide bf16 rows
 constexpr int LDA = C + 4;   // padded row stride of the float32 A matrix
+constexpr int NTHR = 512;    // 4 prep wavefronts + 4 chain wavefronts
 // LDS carve-up (bytes)
 constexpr int OFF_K = 0;                              // K rows          [C][LDK]   bf16
 constexpr int OFF_Q = OFF_K + C * LDK * 2;            // Q rows          [C][LDK]   bf16
 constexpr int OFF_KT = OFF_Q + C * LDK * 2;           // decayed K^T     [DK][LDC]  bf16
 constexpr int OFF_V = OFF_KT + DK * LDC * 2;          // V tile rows     [C][LDC]   bf16
 constexpr int OFF_ST = OFF_V + C * LDC * 2;           // S^T tile        [DVT][LDK] bf16
-constexpr int OFF_XT = OFF_ST + DVT * LDK * 2;        // X^T             [DVT][LDC] bf16
+constexpr int OFF_XT = OFF_ST + DVT * LDK * 2;        // X^T; then output rows [DVT][LDC] bf16
 constexpr int OFF_VNT = OFF_XT + DVT * LDC * 2;       // Vnew^T          [DVT][LDC] bf16
-constexpr int OFF_T = OFF_VNT + DVT * LDC * 2;        // T rows          [C][LDC]   bf16
-constexpr int OFF_P = OFF_T + C * LDC * 2;            // P rows          [C][LDC]   bf16
+constexpr int OFF_P = OFF_VNT + DVT * LDC * 2;        // P rows          [C][LDC]   bf16
 constexpr int OFF_A = OFF_P + C * LDC * 2;            // A rows          [C][LDA]   f32
-constexpr int OFF_TD = OFF_A + C * LDA * 4;           // T block dumps   [3][4][64] f32x4
-constexpr int OFF_BG = OFF_TD + 3 * 4 * 64 * 16;      // beta, g         [2][C]     f32
+constexpr int OFF_TD = OFF_A + C * LDA * 4;           // transposed diagonal inverse blocks [4][64] f32x4
+constexpr int OFF_BG = OFF_TD + 4 * 64 * 16;          // beta, g         [2][C]     f32
 constexpr int LDS_BYTES = OFF_BG + 2 * C * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 }  // namespace mk
 
-__global__ __launch_bounds__(256) void chunk_mfma_kernel(ChunkParams p, int units)
+// One chunk step, three phases separated by workgroup barriers:
+//  1. prep waves (0-3): Gram products K K^T (row block w) and Q K^T (row block
+//     3 - w, which balances the triangular work), the masks that turn them
+//     into A and P, and the inverse T_ww of the diagonal block (I + A_ww);
+//     chain waves (4-7): K S and Q S for row block w, X, and the decayed K^T.
+//  2. chain wave w solves (I + A) Vnew = X for column tile w by block forward
+//     substitution, Vnew_i = T_ii (X_i - sum_{j<i} A_ij Vnew_j), in registers;
+//     prep waves write their share of the next chunk (loaded a whole step
+//     earlier) into LDS and start the loads of the chunk after it.
+//  3. chain waves: outputs, staged through LDS for 16-byte stores;
+//     prep waves: the state update, held in their float32 accumulators.
+// The two roles share every SIMD (wave i runs on SIMD i mod 4), so one role's
+// waits overlap the other's matrix work. Every product loop reads each
+// 16x32 operand fragment from LDS once and reuses it across output tiles.
+__global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
     using namespace mk;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -106,7 +118,6 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(ChunkParams p, int unit
     __bf16 *STs = reinterpret_cast<__bf16 *>(smem + OFF_ST);
     __bf16 *XTs = reinterpret_cast<__bf16 *>(smem + OFF_XT);
     __bf16 *VNTs = reinterpret_cast<__bf16 *>(smem + OFF_VNT);
-    __bf16 *Ts = reinterpret_cast<__bf16 *>(smem + OFF_T);
     __bf16 *Ps = reinterpret_cast<__bf16 *>(smem + OFF_P);
     float *As = reinterpret_cast<float *>(smem + OFF_A);
     f32x4_t *TD = reinterpret_cast<f32x4_t *>(smem + OFF_TD);
@@ -131,11 +142,13 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(ChunkParams p, int unit
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = uniform(tid >> 6);
+    const int wv = uniform(tid >> 6);
+    const bool prep = wv < 4;
+    const int w = wv & 3;
     const int n = lane & 15;   // column within a 16x16 tile
     const int g4 = lane >> 4;  // 4-row group within a 16x16 tile
 
-    int L = p.lens ? p.lens[b] : S;
+    int L = p.lens ? ld_const(p.lens, b) : S;
     L = L < 0 ? 0 : (L > S ? S : L);
 
     const bf16_t *qb = static_cast<const bf16_t *>(p.q) + ((size_t)b * Nk + kh) * S * DK;
@@ -146,66 +159,98 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(ChunkParams p, int unit
     bf16_t *ob = static_cast<bf16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV + col0;
     const bf16_t *ib = p.init ? static_cast<const bf16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
     bf16_t *fb = static_cast<bf16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
+    const int nchunks = (L + C - 1) / C;
 
-    // State slice owned by this wave: key rows [32w, 32w + 32) x the tile's
-    // DVT columns, as 2 x 4 MFMA accumulator tiles: st[rt][ct][i] holds
-    // S[32w + 16rt + 4*g4 + i][16ct + n].
+    // The upper blocks of P stay zero for the whole kernel.
+    for (int e = tid; e < C * LDC; e += NTHR) Ps[e] = (__bf16)0.f;
+
+    // State slice of prep wave w: key rows [32w, 32w + 32) x the tile's DVT
+    // columns as 2 x 4 accumulator tiles, st[rt][ct][i] = S[32w+16rt+4g4+i][16ct+n].
     f32x4_t st[2][DVT / 16];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < DVT / 16; ++ct) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int dk = 32 * w + 16 * rt + 4 * g4 + i;
-                st[rt][ct][i] = ib ? to_f32(ib[(size_t)dk * DV + 16 * ct + n]) : 0.f;
-            }
-        }
-
-    // T's blocks above the diagonal stay zero for the whole kernel.
-    for (int e = tid; e < C * LDC; e += 256) Ts[e] = (__bf16)0.f;
-
-    // S^T (bf16) for the first chunk's products.
-    auto write_st = [&]() {
+    auto write_st = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int ct = 0; ct < DVT / 16; ++ct)
                 *reinterpret_cast<bf16x4_t *>(STs + (16 * ct + n) * LDK + 32 * w + 16 * rt + 4 * g4) = to_bf4(st[rt][ct]);
     };
-    write_st();
+    if (prep) {
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < DVT / 16; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int dk = 32 * w + 16 * rt + 4 * g4 + i;
+                    st[rt][ct][i] = ib ? to_f32(ib[(size_t)dk * DV + 16 * ct + n]) : 0.f;
+                }
+        write_st();
+    }
 
-    const int nchunks = (L + C - 1) / C;
-    for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int nval = min(C, L - t0);
-
-        // ---- load the chunk (rows past the valid length become zeros) ----
+    // Chunk inputs in flight, loaded by the prep waves (256 threads): this
+    // thread's 16-byte pieces of K, Q (4 each) and V (2), and one raw beta / g
+    // value (converted when staged). Rows past the valid length load as zeros.
+    constexpr int NPR = 256;
+    u32x4_t rk[4], rq[4], rv[2];
+    uint32_t rbg = 0;
+    auto issue = [&](int c) __attribute__((always_inline)) {
+        const int t0 = c * C, nv = min(C, L - t0);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int id = tid + 256 * m;
+            const int id = tid + NPR * m;             // 1024 pieces: 64 rows x 16
             const int row = id >> 4, cv = (id & 15) * 8;
-            uint4 kv4 = make_uint4(0, 0, 0, 0), qv4 = make_uint4(0, 0, 0, 0);
-            if (row < nval) {
-                kv4 = *reinterpret_cast<const uint4 *>(kb + (size_t)(t0 + row) * DK + cv);
-                qv4 = *reinterpret_cast<const uint4 *>(qb + (size_t)(t0 + row) * DK + cv);
+            rk[m] = u32x4_t{0u, 0u, 0u, 0u};
+            rq[m] = u32x4_t{0u, 0u, 0u, 0u};
+            if (row < nv) {
+                rk[m] = *reinterpret_cast<const u32x4_t *>(kb + (size_t)(t0 + row) * DK + cv);
+                rq[m] = *reinterpret_cast<const u32x4_t *>(qb + (size_t)(t0 + row) * DK + cv);
             }
-            *reinterpret_cast<uint4 *>(Ks + row * LDK + cv) = kv4;
-            *reinterpret_cast<uint4 *>(Qs + row * LDK + cv) = qv4;
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int id = tid + 256 * m;
+            const int id = tid + NPR * m;             // 512 pieces: 64 rows x 8
             const int row = id >> 3, cv = (id & 7) * 8;
-            uint4 v4 = make_uint4(0, 0, 0, 0);
-            if (row < nval) v4 = *reinterpret_cast<const uint4 *>(vb + (size_t)(t0 + row) * DV + cv);
-            *reinterpret_cast<uint4 *>(Vs + row * LDC + cv) = v4;
+            rv[m] = u32x4_t{0u, 0u, 0u, 0u};
+            if (row < nv) rv[m] = *reinterpret_cast<const u32x4_t *>(vb + (size_t)(t0 + row) * DV + cv);
         }
+        rbg = 0;
         if (tid < C) {
-            betas[tid] = tid < nval ? to_f32(betab[t0 + tid]) : 0.f;
-            gs[tid] = (gb && tid < nval) ? gb[t0 + tid] : 0.f;
+            if (tid < nv) rbg = betab[t0 + tid];
+        } else if (tid < 2 * C) {
+            if (gb && tid - C < nv) rbg = reinterpret_cast<const uint32_t *>(gb)[t0 + tid - C];
         }
-        __syncthreads();
+    };
+    auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int id = tid + NPR * m;
+            const int row = id >> 4, cv = (id & 15) * 8;
+            *reinterpret_cast<u32x4_t *>(Ks + row * LDK + cv) = rk[m];
+            *reinterpret_cast<u32x4_t *>(Qs + row * LDK + cv) = rq[m];
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int id = tid + NPR * m;
+            *reinterpret_cast<u32x4_t *>(Vs + (id >> 3) * LDC + (id & 7) * 8) = rv[m];
+        }
+        if (tid < C) betas[tid] = __uint_as_float(rbg << 16);         // bf16 -> f32
+        else if (tid < 2 * C) betas[tid] = __uint_as_float(rbg);      // betas[C + t] is g[t]
+    };
+
+    if (prep && nchunks > 0) {
+        issue(0);
+        stage();
+        if (nchunks > 1) issue(1);
+    }
+    __syncthreads();
+
+    // The two roles run separate loops with the same three barriers per
+    // chunk (barriers count waves, so they meet); this keeps each role's
+    // registers to its own.
+    if (prep) {
+        for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const int nval = min(C, L - t0);
 
         // ---- in-chunk cumulative log decay (every wave, lane t = token t) ----
         float gam = gs[lane];
@@ -217,77 +262,65 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(ChunkParams p, int unit
         const float gamC = __shfl(gam, 63);
         const float bet = betas[lane];
 
-        // ---- decayed K^T: KT[dk][t] = exp(gamC - gam_t) K[t][dk] ----
+            {
+            // Gram K K^T for row block w (tiles j <= w) and Q K^T for row block
+            // wq = 3 - w (tiles j <= wq); both use the K rows of block j as the
+            // right-hand operand, read once per k-step.
+            const int wq = 3 - w;
+            f32x4_t gk[4], gq[4];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int id = tid + 256 * m;           // 512 items: 32 token pairs x 16 key groups
-            const int tp = (id & 31) * 2, dg = (id >> 5) * 8;
-            const float e0 = __expf(gamC - __shfl(gam, tp));
-            const float e1 = __expf(gamC - __shfl(gam, tp + 1));
-            const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t *>(Ks + tp * LDK + dg);
-            const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t *>(Ks + (tp + 1) * LDK + dg);
+            for (int j = 0; j < 4; ++j) { gk[j] = zero4(); gq[j] = zero4(); }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                __bf16 pr[2];
-                pr[0] = (__bf16)((float)k0[i] * e0);
-                pr[1] = (__bf16)((float)k1[i] * e1);
-                *reinterpret_cast<uint32_t *>(KTs + (dg + i) * LDC + tp) = *reinterpret_cast<uint32_t *>(pr);
-            }
-        }
-
-        // Per-lane row / column decay factors for this wave's 16-row block.
-        float gr[4], br[4], egr[4];
+            for (int s = 0; s < DK / 32; ++s) {
+                const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * w + n) * LDK + 32 * s + 8 * g4);
+                const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(Qs + (16 * wq + n) * LDK + 32 * s + 8 * g4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * w + 4 * g4 + i;
-            gr[i] = __shfl(gam, r);
-            br[i] = __shfl(bet, r);
-            egr[i] = __expf(gr[i]);
-        }
-
-        // ---- Gram products: K K^T and Q K^T for row block w ----
-        f32x4_t gk[4], gq[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { gk[j] = zero4(); gq[j] = zero4(); }
-#pragma unroll
-        for (int s = 0; s < DK / 32; ++s) {
-            const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * w + n) * LDK + 32 * s + 8 * g4);
-            const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(Qs + (16 * w + n) * LDK + 32 * s + 8 * g4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bf16x8_t bk = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * j + n) * LDK + 32 * s + 8 * g4);
-                gk[j] = mma32(ak, bk, gk[j]);
-                gq[j] = mma32(aq, bk, gq[j]);
-            }
-        }
-        // Masks and decays: A (strict lower, beta-weighted), P (lower incl. diagonal).
-        f32x4_t adiag = zero4(), adiagT = zero4();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int cidx = 16 * j + n;
-            const float gc = __shfl(gam, cidx);
-            const float bc = __shfl(bet, cidx);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * w + 4 * g4 + i;
-                const float dec = (cidx <= r) ? __expf(gr[i] - gc) : 0.f;
-                Ps[r * LDC + cidx] = (__bf16)(dec * gq[j][i]);
-                const float a = (cidx < r) ? br[i] * dec * gk[j][i] : 0.f;
-                if (j < w) As[r * LDA + cidx] = a;
-                if (j == w) {
-                    adiag[i] = a;
-                    // transpose of the diagonal block: A[c][r] = beta_c exp(gam_c - gam_r) (k_c . k_r)
-                    adiagT[i] = (r < cidx) ? bc * __expf(gc - gr[i]) * gk[j][i] : 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    if (j > w && j > wq) continue;
+                    const bf16x8_t bk = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * j + n) * LDK + 32 * s + 8 * g4);
+                    if (j <= w) gk[j] = mma32(ak, bk, gk[j]);
+                    if (j <= wq) gq[j] = mma32(aq, bk, gq[j]);
                 }
             }
-        }
-
-        // ---- T_ww = (I + A_ww)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) ----
-        // In the 16x16 accumulator layout a lane holds X[4*g4 + i][n]; that is
-        // the right-hand operand layout of X and the left-hand operand layout
-        // of X^T, so mma16(lay(X^T), lay(Y)) = lay(X Y).
-        f32x4_t tww, twwT;
-        {
+            float gr[4], br[4], gqr[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gr[i] = __shfl(gam, 16 * w + 4 * g4 + i);
+                br[i] = __shfl(bet, 16 * w + 4 * g4 + i);
+                gqr[i] = __shfl(gam, 16 * wq + 4 * g4 + i);
+            }
+            f32x4_t adiag = zero4(), adiagT = zero4();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int cidx = 16 * j + n;
+                const float gc = __shfl(gam, cidx);
+                const float bc = __shfl(bet, cidx);
+                if (j <= w) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * w + 4 * g4 + i;
+                        const float a = (cidx < r) ? br[i] * __expf(gr[i] - gc) * gk[j][i] : 0.f;
+                        if (j < w) As[r * LDA + cidx] = a;
+                        else {
+                            adiag[i] = a;
+                            // transpose of the diagonal block: A[c][r] = beta_c exp(gam_c - gam_r) (k_c . k_r)
+                            adiagT[i] = (r < cidx) ? bc * __expf(gc - gr[i]) * gk[j][i] : 0.f;
+                        }
+                    }
+                }
+                if (j <= wq) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 16 * wq + 4 * g4 + i;
+                        Ps[r * LDC + cidx] = (__bf16)((cidx <= r) ? __expf(gqr[i] - gc) * gq[j][i] : 0.f);
+                    }
+                }
+            }
+            // T_ww = (I + A_ww)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8). In the
+            // 16x16 accumulator layout a lane holds X[4*g4 + i][n]; that is the
+            // right-hand operand layout of X and the left-hand operand layout of
+            // X^T, so mma16(lay(X^T), lay(Y)) = lay(X Y). The substitution needs
+            // T_ww as a left-hand operand, i.e. lay(T_ww^T).
             f32x4_t eye;
 #pragma unroll
             for (int i = 0; i < 4; ++i) eye[i] = (4 * g4 + i == n) ? 1.f : 0.f;
@@ -300,144 +333,189 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(ChunkParams p, int unit
             const bf16x4_t a4b = to_bf4(a4), a4tb = to_bf4(a4t);
             const f32x4_t a8 = mma16(a4tb, a4b, zero4());
             const bf16x4_t x1t = to_bf4(eye - adiagT), y1 = to_bf4(eye + a2);
-            const f32x4_t b1 = mma16(x1t, y1, zero4());          // (I - A)(I + A^2)
-            const f32x4_t b1t = mma16(y1, x1t, zero4());         // its transpose
+            const f32x4_t b1t = mma16(y1, x1t, zero4());         // ((I - A)(I + A^2))^T
             const bf16x4_t b1tb = to_bf4(b1t), y2 = to_bf4(eye + a4);
             const f32x4_t b2t = mma16(y2, b1tb, zero4());        // ((I-A)(I+A^2)(I+A^4))^T
             const bf16x4_t b2tb = to_bf4(b2t), y3 = to_bf4(eye + a8);
-            tww = mma16(b2tb, y3, zero4());
-            twwT = mma16(y3, b2tb, zero4());
-            (void)b1;
-        }
-        const bf16x4_t twwTb = to_bf4(twwT);
-        TD[(0 * 4 + w) * 64 + lane] = tww;
+            TD[w * 64 + lane] = mma16(y3, b2tb, zero4());        // lay(T_ww^T)
+            }
+            __syncthreads();
+            {
+            if (c + 1 < nchunks) stage();
+            if (c + 2 < nchunks) issue(c + 2);
+            }
+            __syncthreads();
+            {
+            // S <- exp(gamC) S + (decayed K)^T Vnew, key rows [32w, 32w+32).
+            const float egC = __expf(gamC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Ts[(16 * w + 4 * g4 + i) * LDC + 16 * w + n] = (__bf16)tww[i];
-        __syncthreads();
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < DVT / 16; ++ct) st[rt][ct] *= egC;
+#pragma unroll
+            for (int s = 0; s < C / 32; ++s) {
+                bf16x8_t ak[2], bv[DVT / 16];
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+                    ak[rt] = *reinterpret_cast<const bf16x8_t *>(KTs + (32 * w + 16 * rt + n) * LDC + 32 * s + 8 * g4);
+#pragma unroll
+                for (int ct = 0; ct < DVT / 16; ++ct)
+                    bv[ct] = *reinterpret_cast<const bf16x8_t *>(VNTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < DVT / 16; ++ct) st[rt][ct] = mma32(ak[rt], bv[ct], st[rt][ct]);
+            }
+            write_st();
+            }
+            __syncthreads();
+        }
+    } else {
+        f32x4_t yq[DVT / 16];   // exp(gam) Q S for the output
+        for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        const int nval = min(C, L - t0);
 
-        // ---- off-diagonal blocks of T, one block diagonal per step ----
-        // A-operand of A_wm: lane holds A[16w + n][16m + 4*g4 .. +3].
-        auto a_op = [&](int m) {
-            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(As + (16 * w + n) * LDA + 16 * m + 4 * g4);
-            return to_bf4(v);
-        };
-        if (w >= 1) {   // T_{w,w-1} = -T_ww A_{w,w-1} T_{w-1,w-1}
-            const f32x4_t mwm = mma16(a_op(w - 1), to_bf4(TD[(0 * 4 + w - 1) * 64 + lane]), zero4());
-            const f32x4_t t1 = -mma16(twwTb, to_bf4(mwm), zero4());
-            TD[(1 * 4 + w) * 64 + lane] = t1;
+        // ---- in-chunk cumulative log decay (every wave, lane t = token t) ----
+        float gam = gs[lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[(16 * w + 4 * g4 + i) * LDC + 16 * (w - 1) + n] = (__bf16)t1[i];
+        for (int d = 1; d < 64; d <<= 1) {
+            const float y = __shfl_up(gam, d);
+            if (lane >= d) gam += y;
         }
-        __syncthreads();
-        if (w >= 2) {   // T_{w,w-2} = -T_ww (A_{w,w-2} T_{w-2,w-2} + A_{w,w-1} T_{w-1,w-2})
-            f32x4_t mwm = mma16(a_op(w - 2), to_bf4(TD[(0 * 4 + w - 2) * 64 + lane]), zero4());
-            mwm = mma16(a_op(w - 1), to_bf4(TD[(1 * 4 + w - 1) * 64 + lane]), mwm);
-            const f32x4_t t2 = -mma16(twwTb, to_bf4(mwm), zero4());
-            TD[(2 * 4 + w) * 64 + lane] = t2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[(16 * w + 4 * g4 + i) * LDC + 16 * (w - 2) + n] = (__bf16)t2[i];
-        }
-        __syncthreads();
-        if (w == 3) {   // T_30 = -T_33 (A_30 T_00 + A_31 T_10 + A_32 T_20)
-            f32x4_t mwm = mma16(a_op(0), to_bf4(TD[(0 * 4 + 0) * 64 + lane]), zero4());
-            mwm = mma16(a_op(1), to_bf4(TD[(1 * 4 + 1) * 64 + lane]), mwm);
-            mwm = mma16(a_op(2), to_bf4(TD[(2 * 4 + 2) * 64 + lane]), mwm);
-            const f32x4_t t3 = -mma16(twwTb, to_bf4(mwm), zero4());
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[(16 * w + 4 * g4 + i) * LDC + n] = (__bf16)t3[i];
-        }
+        const float gamC = __shfl(gam, 63);
+        const float bet = betas[lane];
 
-        // ---- K S and Q S for row block w; X = beta (V - exp(gam) K S) ----
-        f32x4_t yq[DVT / 16];
+            {
+            // K S and Q S for row block w; X = beta (V - exp(gam) K S).
+            float brr[4], egr[4];
 #pragma unroll
-        for (int ct = 0; ct < DVT / 16; ++ct) {
-            f32x4_t yk = zero4();
-            yq[ct] = zero4();
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * w + 4 * g4 + i;
+                brr[i] = __shfl(bet, r);
+                egr[i] = __expf(__shfl(gam, r));
+            }
+            f32x4_t yk[DVT / 16];
+#pragma unroll
+            for (int ct = 0; ct < DVT / 16; ++ct) { yk[ct] = zero4(); yq[ct] = zero4(); }
 #pragma unroll
             for (int s = 0; s < DK / 32; ++s) {
                 const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * w + n) * LDK + 32 * s + 8 * g4);
                 const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(Qs + (16 * w + n) * LDK + 32 * s + 8 * g4);
-                const bf16x8_t bs = *reinterpret_cast<const bf16x8_t *>(STs + (16 * ct + n) * LDK + 32 * s + 8 * g4);
-                yk = mma32(ak, bs, yk);
-                yq[ct] = mma32(aq, bs, yq[ct]);
-            }
-            f32x4_t x;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * w + 4 * g4 + i;
-                const float vv = (float)Vs[r * LDC + 16 * ct + n];
-                x[i] = br[i] * (vv - egr[i] * yk[i]);
-            }
-            *reinterpret_cast<bf16x4_t *>(XTs + (16 * ct + n) * LDC + 16 * w + 4 * g4) = to_bf4(x);
-        }
-        __syncthreads();
-
-        // ---- Vnew = T X (rows of block w need T columns < 16(w+1)) ----
-        const int ksteps = w >= 2 ? 2 : 1;
-#pragma unroll
-        for (int ct = 0; ct < DVT / 16; ++ct) {
-            f32x4_t vn = zero4();
-            for (int s = 0; s < ksteps; ++s) {
-                const bf16x8_t at = *reinterpret_cast<const bf16x8_t *>(Ts + (16 * w + n) * LDC + 32 * s + 8 * g4);
-                const bf16x8_t bx = *reinterpret_cast<const bf16x8_t *>(XTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
-                vn = mma32(at, bx, vn);
-            }
-            *reinterpret_cast<bf16x4_t *>(VNTs + (16 * ct + n) * LDC + 16 * w + 4 * g4) = to_bf4(vn);
-        }
-        __syncthreads();
-
-        // ---- O = scale (exp(gam) Q S + P Vnew), rows of block w ----
-#pragma unroll
-        for (int ct = 0; ct < DVT / 16; ++ct) {
-            f32x4_t o = zero4();
-            for (int s = 0; s < ksteps; ++s) {
-                const bf16x8_t ap = *reinterpret_cast<const bf16x8_t *>(Ps + (16 * w + n) * LDC + 32 * s + 8 * g4);
-                const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(VNTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
-                o = mma32(ap, bv, o);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * w + 4 * g4 + i;
-                const int t = t0 + r;
-                if (t < S) {
-                    const float val = r < nval ? p.scale * (egr[i] * yq[ct][i] + o[i]) : 0.f;
-                    ob[(size_t)t * DV + 16 * ct + n] = from_f32<bf16_t>(val);
+                for (int ct = 0; ct < DVT / 16; ++ct) {
+                    const bf16x8_t bs = *reinterpret_cast<const bf16x8_t *>(STs + (16 * ct + n) * LDK + 32 * s + 8 * g4);
+                    yk[ct] = mma32(ak, bs, yk[ct]);
+                    yq[ct] = mma32(aq, bs, yq[ct]);
                 }
             }
-        }
-
-        // ---- S <- exp(gamC) S + (decayed K)^T Vnew, key rows [32w, 32w+32) ----
-        const float egC = __expf(gamC);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int ct = 0; ct < DVT / 16; ++ct) {
-                f32x4_t acc = st[rt][ct] * egC;
+                f32x4_t x;
 #pragma unroll
-                for (int s = 0; s < C / 32; ++s) {
-                    const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(KTs + (32 * w + 16 * rt + n) * LDC + 32 * s + 8 * g4);
-                    const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(VNTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
-                    acc = mma32(ak, bv, acc);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * w + 4 * g4 + i;
+                    const float vv = (float)Vs[r * LDC + 16 * ct + n];
+                    x[i] = brr[i] * (vv - egr[i] * yk[ct][i]);
+                    yq[ct][i] *= egr[i];
                 }
-                st[rt][ct] = acc;
+                *reinterpret_cast<bf16x4_t *>(XTs + (16 * ct + n) * LDC + 16 * w + 4 * g4) = to_bf4(x);
             }
-        write_st();
-        __syncthreads();
+            // decayed K^T: KT[dk][t] = exp(gamC - gam_t) K[t][dk] (256 chain threads, 512 items)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int id = (tid - 256) + 256 * m;   // 32 token pairs x 16 key groups
+                const int tp = (id & 31) * 2, dg = (id >> 5) * 8;
+                const float e0 = __expf(gamC - __shfl(gam, tp));
+                const float e1 = __expf(gamC - __shfl(gam, tp + 1));
+                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t *>(Ks + tp * LDK + dg);
+                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t *>(Ks + (tp + 1) * LDK + dg);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __bf16 pr[2];
+                    pr[0] = (__bf16)((float)k0[i] * e0);
+                    pr[1] = (__bf16)((float)k1[i] * e1);
+                    *reinterpret_cast<uint32_t *>(KTs + (dg + i) * LDC + tp) = *reinterpret_cast<uint32_t *>(pr);
+                }
+            }
+            }
+            __syncthreads();
+            {
+            // (I + A) Vnew = X for column tile ct = w, row block by row block:
+            // Vnew_i = T_ii (X_i - sum_{j<i} A_ij Vnew_j). Left-hand operand
+            // of -A_ij: lane holds -A[16i + n][16j + 4*g4 .. +3].
+            const int ct = w;
+            auto naop = [&](int i, int j) __attribute__((always_inline)) {
+                return to_bf4(-*reinterpret_cast<const f32x4_t *>(As + (16 * i + n) * LDA + 16 * j + 4 * g4));
+            };
+            bf16x4_t vnb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x4_t xb = *reinterpret_cast<const bf16x4_t *>(XTs + (16 * ct + n) * LDC + 16 * i + 4 * g4);
+                f32x4_t acc;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = (float)xb[e];
+#pragma unroll
+                for (int j = 0; j < i; ++j) acc = mma16(naop(i, j), vnb[j], acc);
+                const f32x4_t vn = mma16(to_bf4(TD[i * 64 + lane]), to_bf4(acc), zero4());
+                vnb[i] = to_bf4(vn);
+                *reinterpret_cast<bf16x4_t *>(VNTs + (16 * ct + n) * LDC + 16 * i + 4 * g4) = vnb[i];
+            }
+            }
+            __syncthreads();
+            {
+            // O = scale (exp(gam) Q S + P Vnew) for row block w, staged through
+            // this wave's part of the X^T buffer as rows, then stored 16 bytes
+            // at a time.
+            const int ks = w >= 2 ? 2 : 1;
+            f32x4_t o[DVT / 16];
+#pragma unroll
+            for (int ct = 0; ct < DVT / 16; ++ct) o[ct] = yq[ct];
+            for (int s = 0; s < ks; ++s) {
+                const bf16x8_t ap = *reinterpret_cast<const bf16x8_t *>(Ps + (16 * w + n) * LDC + 32 * s + 8 * g4);
+#pragma unroll
+                for (int ct = 0; ct < DVT / 16; ++ct) {
+                    const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(VNTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
+                    o[ct] = mma32(ap, bv, o[ct]);
+                }
+            }
+            __bf16 *Os = XTs;   // rows [16w, 16w + 16) of a [C][LDC] row-major view
+#pragma unroll
+            for (int ct = 0; ct < DVT / 16; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * w + 4 * g4 + i;
+                    Os[r * LDC + 16 * ct + n] = (__bf16)(r < nval ? p.scale * o[ct][i] : 0.f);
+                }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int id = lane + 64 * m;             // 16 rows x 8 pieces
+                const int r = 16 * w + (id >> 3), cv = (id & 7) * 8;
+                if (t0 + r < S)
+                    *reinterpret_cast<uint4 *>(ob + (size_t)(t0 + r) * DV + cv) =
+                        *reinterpret_cast<const uint4 *>(Os + r * LDC + cv);
+            }
+            }
+            __syncthreads();
+        }
     }
 
     // Final state of this tile, then zeros for every output row past the
     // last processed chunk.
+    if (prep) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < DVT / 16; ++ct)
+            for (int ct = 0; ct < DVT / 16; ++ct)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int dk = 32 * w + 16 * rt + 4 * g4 + i;
-                fb[(size_t)dk * DV + 16 * ct + n] = from_f32<bf16_t>(st[rt][ct][i]);
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int dk = 32 * w + 16 * rt + 4 * g4 + i;
+                    fb[(size_t)dk * DV + 16 * ct + n] = from_f32<bf16_t>(st[rt][ct][i]);
+                }
+    }
     const int tz = nchunks * C;
-    for (int id = tid; id < (S - tz) * (DVT / 8); id += 256) {
+    for (int id = tid; id < (S - tz) * (DVT / 8); id += NTHR) {
         const int row = tz + id / (DVT / 8), cv = (id % (DVT / 8)) * 8;
         *reinterpret_cast<uint4 *>(ob + (size_t)row * DV + cv) = make_uint4(0, 0, 0, 0);
     }
@@ -571,7 +649,7 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
                 if (e != hipSuccess) return e;
                 attr_done.store(1, std::memory_order_release);
             }
-            return hipLaunchKernel((const void *)chunk_mfma_kernel, dim3(nwg), dim3(256), args, mk::LDS_BYTES, s);
+            return hipLaunchKernel((const void *)chunk_mfma_kernel, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);
         }
         *supported = false;
         return hipSuccess;
