@@ -34,6 +34,7 @@
 //  * chunk_f32_kernel — float32 I/O, small heads. The same chunk algorithm in
 //    plain float32 arithmetic; T by row-wise forward substitution.
 #include <atomic>
+#include <type_traits>
 
 #include "gdr_common.h"
 
@@ -43,6 +44,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
 {
@@ -67,65 +69,160 @@ __device__ __forceinline__ f32x4_t zero4()
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// v_mfma_f32_32x32x16_bf16. Lane l (h = l / 32) supplies row l % 32 of the
+// left operand and column l % 32 of the right one, each as 8 consecutive
+// k-values starting at 8h; the result gives lane l column l % 32, register q
+// holding row 8(q / 4) + 4h + q % 4.
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t zero16()
+{
+    f32x16_t z;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) z[q] = 0.f;
+    return z;
+}
+// Row of result register q for a lane in half hh of the wave.
+__device__ __forceinline__ int drow(int q, int hh) { return 8 * (q >> 2) + 4 * hh + (q & 3); }
+
+// Registers 8s..8s+7 of a 32x32 result D(X), rounded to bf16, are the
+// operand of k-step s when the contraction runs over the rows of X: the right
+// operand of X and the left operand of X^T. This fixes the order in which a
+// k-step visits its 16 contraction indices: storage slot 8h + e holds index
+// 4h + e % 4 + 8(e / 4), i.e. bits 2 and 3 of the index are swapped ("k-order").
+// Every operand tile in LDS is kept in k-order along its contraction axis, so
+// each lane reads or writes one 16-byte piece per k-step.
+__device__ __forceinline__ bf16x8_t op8(const f32x16_t &d, int s)
+{
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)d[8 * s + e];
+    return r;
+}
+// D(X Y) + c over a 32-long contraction, from D(X^T) and D(Y).
+__device__ __forceinline__ f32x16_t prod(const f32x16_t &dxt, const f32x16_t &dy, f32x16_t c)
+{
+    c = mfma32(op8(dxt, 0), op8(dy, 0), c);
+    return mfma32(op8(dxt, 1), op8(dy, 1), c);
+}
+
+// Byte offset of 16-byte piece u of row r in a tile of 256- or 128-byte rows.
+// The XOR swizzle spreads the 16 rows read by a half-wave over all 16 bank
+// groups, so operand reads and result writes are free of bank conflicts.
+__device__ __forceinline__ int sw256(int r, int u) { return (r << 8) + ((u ^ (r & 15)) << 4); }
+__device__ __forceinline__ int sw128(int r, int u) { return (r << 7) + ((u ^ ((r >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ bf16x8_t ld8(const unsigned char *base, int off)
+{
+    return *reinterpret_cast<const bf16x8_t *>(base + off);
+}
+__device__ __forceinline__ void st8(unsigned char *base, int off, bf16x8_t v)
+{
+    *reinterpret_cast<bf16x8_t *>(base + off) = v;
+}
+
 namespace mk {
-constexpr int C = 64;        // chunk length
-constexpr int DK = 128;      // key head size
-constexpr int DV = 128;      // value head size
-constexpr int DVT = 64;      // value columns per workgroup
-constexpr int NT = DV / DVT; // column tiles per head
-constexpr int LDK = DK + 8;  // padded row stride (elements) of 128-wide bf16 rows
-constexpr int LDC = C + 8;   // padded row stride of 64-wide bf16 rows
-constexpr int LDA = C + 4;   // padded row stride of the float32 A matrix
-constexpr int NTHR = 512;    // 4 prep wavefronts + 4 chain wavefronts
-// LDS carve-up (bytes)
-constexpr int OFF_K = 0;                              // K rows          [C][LDK]   bf16
-constexpr int OFF_Q = OFF_K + C * LDK * 2;            // Q rows          [C][LDK]   bf16
-constexpr int OFF_KT = OFF_Q + C * LDK * 2;           // decayed K^T     [DK][LDC]  bf16
-constexpr int OFF_V = OFF_KT + DK * LDC * 2;          // V tile rows     [C][LDC]   bf16
-constexpr int OFF_ST = OFF_V + C * LDC * 2;           // S^T tile        [DVT][LDK] bf16
-constexpr int OFF_XT = OFF_ST + DVT * LDK * 2;        // X^T; then output rows [DVT][LDC] bf16
-constexpr int OFF_VNT = OFF_XT + DVT * LDC * 2;       // Vnew^T          [DVT][LDC] bf16
-constexpr int OFF_P = OFF_VNT + DVT * LDC * 2;        // P rows          [C][LDC]   bf16
-constexpr int OFF_A = OFF_P + C * LDC * 2;            // A rows          [C][LDA]   f32
-constexpr int OFF_TD = OFF_A + C * LDA * 4;           // transposed diagonal inverse blocks [4][64] f32x4
-constexpr int OFF_BG = OFF_TD + 4 * 64 * 16;          // beta, g         [2][C]     f32
-constexpr int LDS_BYTES = OFF_BG + 2 * C * 4;
+constexpr int C = 64;          // chunk length
+constexpr int DK = 128;        // key head size
+constexpr int DV = 128;        // value head size
+constexpr int DVT = 64;        // value columns per workgroup
+constexpr int NT = DV / DVT;   // column tiles per head
+constexpr int NPREP = 6;       // wavefronts building the chunk operands
+constexpr int NTHR = 512;      // 6 prep + 2 chain wavefronts
+// Operand set of one chunk (double-buffered: the chain consumes chunk c while
+// the prep waves build chunk c + 1). Byte offsets within a set:
+constexpr int S_Q = 0;         // Q rows, features in k-order             [64][256 B]
+constexpr int S_KT = 16384;    // K^T rows (features), tokens in k-order  [128][128 B]
+constexpr int S_W = 32768;     // -W rows, features in k-order            [64][256 B]; K rows while staging
+constexpr int S_P = 49152;     // P rows, tokens in k-order               [64][128 B]
+constexpr int S_U = 57344;     // U in result-register order, bf16       [2][2][2][64][16 B]; V rows while staging
+constexpr int S_VEC = 65536;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64], exp(gamma_C)
+constexpr int SET_BYTES = 66560;
+// Prep-only buffers.
+constexpr int P_VT = 2 * SET_BYTES;  // V^T rows (value columns), tokens in k-order [64][128 B]
+constexpr int P_TP = P_VT + 8192;    // T diag(beta exp(gamma)) rows, k-order     [64][128 B]
+constexpr int P_TB = P_TP + 8192;    // T diag(beta) rows, k-order                [64][128 B]
+constexpr int P_A10 = P_TB + 8192;   // operand of A_10^T, register order         [2][64][16 B]
+constexpr int P_Z = P_A10 + 2048;    // operand of -(T_11 A_10)^T, register order [2][64][16 B]
+constexpr int P_BG = P_Z + 2048;     // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
+constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
+constexpr int LDS_BYTES = P_FLAG + 64;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 }  // namespace mk
 
-// One chunk step, three phases separated by workgroup barriers:
-//  1. prep waves (0-3): Gram products K K^T (row block w) and Q K^T (row block
-//     3 - w, which balances the triangular work), the masks that turn them
-//     into A and P, and the inverse T_ww of the diagonal block (I + A_ww);
-//     chain waves (4-7): K S and Q S for row block w, X, and the decayed K^T.
-//  2. chain wave w solves (I + A) Vnew = X for column tile w by block forward
-//     substitution, Vnew_i = T_ii (X_i - sum_{j<i} A_ij Vnew_j), in registers;
-//     prep waves write their share of the next chunk (loaded a whole step
-//     earlier) into LDS and start the loads of the chunk after it.
-//  3. chain waves: outputs, staged through LDS for 16-byte stores;
-//     prep waves: the state update, held in their float32 accumulators.
-// The two roles share every SIMD (wave i runs on SIMD i mod 4), so one role's
-// waits overlap the other's matrix work. Every product loop reads each
-// 16x32 operand fragment from LDS once and reuses it across output tiles.
+// Synchronisation inside the workgroup orders LDS only. Waves never pass
+// data through global memory, so a barrier or counter must not wait for the
+// prefetch loads or output stores in flight (a workgroup-scope fence would).
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+// Inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then the totals of rows 0 and 0-1 carried into later rows.
+__device__ __forceinline__ float wave_prefix_sum(float x)
+{
+    x += dpp_f<0x111, 0xf>(x);   // row_shr:1
+    x += dpp_f<0x112, 0xf>(x);   // row_shr:2
+    x += dpp_f<0x114, 0xf>(x);   // row_shr:4
+    x += dpp_f<0x118, 0xf>(x);   // row_shr:8
+    x += dpp_f<0x142, 0xa>(x);   // row_bcast:15 into rows 1 and 3
+    x += dpp_f<0x143, 0xc>(x);   // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Arrival counters (LDS) that order the prep waves among themselves without
+// holding up the chain waves. Counters only grow; a wave waits for the count
+// that the current chunk's arrivals reach. LDS operations of one wave complete
+// in order, so a wave's writes are visible once its increment is.
+__device__ __forceinline__ void arrive(uint32_t *f, int lane)
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_fetch_add(f, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void wait_for(uint32_t *f, uint32_t target)
+{
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");
+}
+
+// One workgroup per (sequence, value head, 64-column tile of Dv); the columns
+// of S evolve independently, so each tile carries its own slice of the state.
+// The chunk step is split so that only two products depend on the state:
+//
+//   W = T diag(beta exp(gamma)) K,  U = T diag(beta) V,  T = (I + A)^-1
+//   Vnew = U - W S0
+//   O^T  = (S0^T Q^T) diag(exp(gamma)) + Vnew^T P^T          (scaled on store)
+//   S    = exp(gamma_C) S0 + K^T diag(exp(gamma_C - gamma)) Vnew
+//
+// Chain waves (6, 7) each own 32 state columns in float32 result registers
+// and run these three products for chunk c; their operands never leave
+// registers except W, Q, P, K^T and U, read from the chunk's operand set.
+// Prep waves (0-5) build the operand set of chunk c + 1 meanwhile:
+//   stage K, Q, V (loaded from HBM one chunk earlier) in k-order;
+//   Gram blocks: wave 0/1 the diagonal blocks of K K^T, wave 2 the block
+//     below them, waves 3-5 the three nonzero blocks of P;
+//   waves 0/1 invert (I + A_dd) as the finite product
+//     (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16) (A_dd is nilpotent of
+//     index 32), then T_10 = -T_11 A_10 T_00 (waves 1 and 0);
+//   waves 2-5 transpose K and V (a product with the identity, exact);
+//   waves 0-3 form W^T = K^T T'^T by 32 features, waves 4/5 U by 32 columns.
+// Chain and prep meet once per chunk at a workgroup barrier.
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
     using namespace mk;
     extern __shared__ __align__(16) unsigned char smem[];
-    __bf16 *Ks = reinterpret_cast<__bf16 *>(smem + OFF_K);
-    __bf16 *Qs = reinterpret_cast<__bf16 *>(smem + OFF_Q);
-    __bf16 *KTs = reinterpret_cast<__bf16 *>(smem + OFF_KT);
-    __bf16 *Vs = reinterpret_cast<__bf16 *>(smem + OFF_V);
-    __bf16 *STs = reinterpret_cast<__bf16 *>(smem + OFF_ST);
-    __bf16 *XTs = reinterpret_cast<__bf16 *>(smem + OFF_XT);
-    __bf16 *VNTs = reinterpret_cast<__bf16 *>(smem + OFF_VNT);
-    __bf16 *Ps = reinterpret_cast<__bf16 *>(smem + OFF_P);
-    float *As = reinterpret_cast<float *>(smem + OFF_A);
-    f32x4_t *TD = reinterpret_cast<f32x4_t *>(smem + OFF_TD);
-    float *betas = reinterpret_cast<float *>(smem + OFF_BG);
-    float *gs = betas + C;
 
     // Workgroup -> unit. Workgroups are dealt round-robin to the 8 XCDs, so
-    // consecutive units (the value heads and column tiles that share one
+    // consecutive units (the column tiles and value heads that share one
     // (b, key head) and therefore the same q/k) go to one XCD and its L2.
     const int nwg = gridDim.x;
     const int u = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
@@ -143,13 +240,12 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = uniform(tid >> 6);
-    const bool prep = wv < 4;
-    const int w = wv & 3;
-    const int n = lane & 15;   // column within a 16x16 tile
-    const int g4 = lane >> 4;  // 4-row group within a 16x16 tile
+    const int hh = lane >> 5;    // half of the wave
+    const int c32 = lane & 31;   // row / column of a 32x32 operand or result
 
     int L = p.lens ? ld_const(p.lens, b) : S;
     L = L < 0 ? 0 : (L > S ? S : L);
+    const int nchunks = (L + C - 1) / C;
 
     const bf16_t *qb = static_cast<const bf16_t *>(p.q) + ((size_t)b * Nk + kh) * S * DK;
     const bf16_t *kb = static_cast<const bf16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
@@ -159,361 +255,432 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     bf16_t *ob = static_cast<bf16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV + col0;
     const bf16_t *ib = p.init ? static_cast<const bf16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
     bf16_t *fb = static_cast<bf16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
-    const int nchunks = (L + C - 1) / C;
 
-    // The upper blocks of P stay zero for the whole kernel.
-    for (int e = tid; e < C * LDC; e += NTHR) Ps[e] = (__bf16)0.f;
+    uint32_t *flags = reinterpret_cast<uint32_t *>(smem + P_FLAG);
+    if (tid < 4) flags[tid] = 0u;
+    lds_barrier();
 
-    // State slice of prep wave w: key rows [32w, 32w + 32) x the tile's DVT
-    // columns as 2 x 4 accumulator tiles, st[rt][ct][i] = S[32w+16rt+4g4+i][16ct+n].
-    f32x4_t st[2][DVT / 16];
-    auto write_st = [&]() __attribute__((always_inline)) {
+    if (wv >= NPREP) {
+        // ------------------------------ chain ------------------------------
+        const int cw = wv - NPREP;   // state columns [32cw, 32cw + 32) of the tile
+        // The recurrence is the critical path: its instructions win issue
+        // arbitration against the prep waves sharing the SIMD.
+        __builtin_amdgcn_s_setprio(2);
+        // Outputs go through a buffer resource bounded by this head's output
+        // plane: stores of rows past S fall outside it and are dropped by the
+        // hardware bounds check, with no branch in the loop.
+        const __amdgpu_buffer_rsrc_t orsrc =
+            __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, (S * DV - col0) * 2, 0x00020000);
+        f32x16_t st[4];              // st[f][q] = S[32f + drow(q)][32cw + c32]
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+        for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct)
-                *reinterpret_cast<bf16x4_t *>(STs + (16 * ct + n) * LDK + 32 * w + 16 * rt + 4 * g4) = to_bf4(st[rt][ct]);
-    };
-    if (prep) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int dk = 32 * w + 16 * rt + 4 * g4 + i;
-                    st[rt][ct][i] = ib ? to_f32(ib[(size_t)dk * DV + 16 * ct + n]) : 0.f;
-                }
-        write_st();
-    }
-
-    // Chunk inputs in flight, loaded by the prep waves (256 threads): this
-    // thread's 16-byte pieces of K, Q (4 each) and V (2), and one raw beta / g
-    // value (converted when staged). Rows past the valid length load as zeros.
-    constexpr int NPR = 256;
-    u32x4_t rk[4], rq[4], rv[2];
-    uint32_t rbg = 0;
-    auto issue = [&](int c) __attribute__((always_inline)) {
-        const int t0 = c * C, nv = min(C, L - t0);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int id = tid + NPR * m;             // 1024 pieces: 64 rows x 16
-            const int row = id >> 4, cv = (id & 15) * 8;
-            rk[m] = u32x4_t{0u, 0u, 0u, 0u};
-            rq[m] = u32x4_t{0u, 0u, 0u, 0u};
-            if (row < nv) {
-                rk[m] = *reinterpret_cast<const u32x4_t *>(kb + (size_t)(t0 + row) * DK + cv);
-                rq[m] = *reinterpret_cast<const u32x4_t *>(qb + (size_t)(t0 + row) * DK + cv);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int id = tid + NPR * m;             // 512 pieces: 64 rows x 8
-            const int row = id >> 3, cv = (id & 7) * 8;
-            rv[m] = u32x4_t{0u, 0u, 0u, 0u};
-            if (row < nv) rv[m] = *reinterpret_cast<const u32x4_t *>(vb + (size_t)(t0 + row) * DV + cv);
-        }
-        rbg = 0;
-        if (tid < C) {
-            if (tid < nv) rbg = betab[t0 + tid];
-        } else if (tid < 2 * C) {
-            if (gb && tid - C < nv) rbg = reinterpret_cast<const uint32_t *>(gb)[t0 + tid - C];
-        }
-    };
-    auto stage = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int id = tid + NPR * m;
-            const int row = id >> 4, cv = (id & 15) * 8;
-            *reinterpret_cast<u32x4_t *>(Ks + row * LDK + cv) = rk[m];
-            *reinterpret_cast<u32x4_t *>(Qs + row * LDK + cv) = rq[m];
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int id = tid + NPR * m;
-            *reinterpret_cast<u32x4_t *>(Vs + (id >> 3) * LDC + (id & 7) * 8) = rv[m];
-        }
-        if (tid < C) betas[tid] = __uint_as_float(rbg << 16);         // bf16 -> f32
-        else if (tid < 2 * C) betas[tid] = __uint_as_float(rbg);      // betas[C + t] is g[t]
-    };
-
-    if (prep && nchunks > 0) {
-        issue(0);
-        stage();
-        if (nchunks > 1) issue(1);
-    }
-    __syncthreads();
-
-    // The two roles run separate loops with the same three barriers per
-    // chunk (barriers count waves, so they meet); this keeps each role's
-    // registers to its own.
-    if (prep) {
+            for (int q = 0; q < 16; ++q)
+                st[f][q] = ib ? to_f32(ib[(size_t)(32 * f + drow(q, hh)) * DV + 32 * cw + c32]) : 0.f;
+        if (nchunks > 0) lds_barrier();   // operand set of chunk 0 is ready
         for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int nval = min(C, L - t0);
+            const unsigned char *set = smem + (c & 1) * SET_BYTES;
+            const int t0 = c * C;
 
-        // ---- in-chunk cumulative log decay (every wave, lane t = token t) ----
-        float gam = gs[lane];
+            bf16x8_t sop[8];
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(gam, d);
-            if (lane >= d) gam += y;
-        }
-        const float gamC = __shfl(gam, 63);
-        const float bet = betas[lane];
+            for (int ks = 0; ks < 8; ++ks) sop[ks] = op8(st[ks >> 1], ks & 1);
 
-            {
-            // Gram K K^T for row block w (tiles j <= w) and Q K^T for row block
-            // wq = 3 - w (tiles j <= wq); both use the K rows of block j as the
-            // right-hand operand, read once per k-step.
-            const int wq = 3 - w;
-            f32x4_t gk[4], gq[4];
+            // Vnew = U - W S0 and S0^T Q^T, one pass over the 128 features.
+            f32x16_t vn[2], ot[2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { gk[j] = zero4(); gq[j] = zero4(); }
+            for (int rb = 0; rb < 2; ++rb) {
+                ot[rb] = zero16();
 #pragma unroll
-            for (int s = 0; s < DK / 32; ++s) {
-                const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * w + n) * LDK + 32 * s + 8 * g4);
-                const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(Qs + (16 * wq + n) * LDK + 32 * s + 8 * g4);
+                for (int q = 0; q < 2; ++q) {
+                    const bf16x8_t uu = ld8(set, S_U + ((cw * 2 + rb) * 2 + q) * 1024 + lane * 16);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (j > w && j > wq) continue;
-                    const bf16x8_t bk = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * j + n) * LDK + 32 * s + 8 * g4);
-                    if (j <= w) gk[j] = mma32(ak, bk, gk[j]);
-                    if (j <= wq) gq[j] = mma32(aq, bk, gq[j]);
+                    for (int e = 0; e < 8; ++e) vn[rb][8 * q + e] = (float)uu[e];
                 }
             }
-            float gr[4], br[4], gqr[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                gr[i] = __shfl(gam, 16 * w + 4 * g4 + i);
-                br[i] = __shfl(bet, 16 * w + 4 * g4 + i);
-                gqr[i] = __shfl(gam, 16 * wq + 4 * g4 + i);
+            for (int ks = 0; ks < 8; ++ks) {
+                const bf16x8_t aw0 = ld8(set, S_W + sw256(c32, 2 * ks + hh));
+                const bf16x8_t aw1 = ld8(set, S_W + sw256(32 + c32, 2 * ks + hh));
+                const bf16x8_t bq0 = ld8(set, S_Q + sw256(c32, 2 * ks + hh));
+                const bf16x8_t bq1 = ld8(set, S_Q + sw256(32 + c32, 2 * ks + hh));
+                vn[0] = mfma32(aw0, sop[ks], vn[0]);
+                vn[1] = mfma32(aw1, sop[ks], vn[1]);
+                ot[0] = mfma32(sop[ks], bq0, ot[0]);
+                ot[1] = mfma32(sop[ks], bq1, ot[1]);
             }
-            f32x4_t adiag = zero4(), adiagT = zero4();
+            const float *vec = reinterpret_cast<const float *>(set + S_VEC);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int cidx = 16 * j + n;
-                const float gc = __shfl(gam, cidx);
-                const float bc = __shfl(bet, cidx);
-                if (j <= w) {
+            for (int tb = 0; tb < 2; ++tb) ot[tb] *= vec[32 * tb + c32];
+
+            // Vnew as the left operand of Vnew^T, and decayed as the right
+            // operand of the state update.
+            bf16x8_t vna[4], vnb[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * w + 4 * g4 + i;
-                        const float a = (cidx < r) ? br[i] * __expf(gr[i] - gc) * gk[j][i] : 0.f;
-                        if (j < w) As[r * LDA + cidx] = a;
-                        else {
-                            adiag[i] = a;
-                            // transpose of the diagonal block: A[c][r] = beta_c exp(gam_c - gam_r) (k_c . k_r)
-                            adiagT[i] = (r < cidx) ? bc * __expf(gc - gr[i]) * gk[j][i] : 0.f;
-                        }
-                    }
+            for (int rb = 0; rb < 2; ++rb) {
+                f32x16_t dv;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float4 d4 = *reinterpret_cast<const float4 *>(vec + 64 + 32 * rb + 8 * m + 4 * hh);
+                    dv[4 * m + 0] = vn[rb][4 * m + 0] * d4.x;
+                    dv[4 * m + 1] = vn[rb][4 * m + 1] * d4.y;
+                    dv[4 * m + 2] = vn[rb][4 * m + 2] * d4.z;
+                    dv[4 * m + 3] = vn[rb][4 * m + 3] * d4.w;
                 }
-                if (j <= wq) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int r = 16 * wq + 4 * g4 + i;
-                        Ps[r * LDC + cidx] = (__bf16)((cidx <= r) ? __expf(gqr[i] - gc) * gq[j][i] : 0.f);
-                    }
+                for (int s = 0; s < 2; ++s) {
+                    vna[2 * rb + s] = op8(vn[rb], s);
+                    vnb[2 * rb + s] = op8(dv, s);
                 }
             }
-            // T_ww = (I + A_ww)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8). In the
-            // 16x16 accumulator layout a lane holds X[4*g4 + i][n]; that is the
-            // right-hand operand layout of X and the left-hand operand layout of
-            // X^T, so mma16(lay(X^T), lay(Y)) = lay(X Y). The substitution needs
-            // T_ww as a left-hand operand, i.e. lay(T_ww^T).
-            f32x4_t eye;
+            // O^T += Vnew^T P^T (P is lower triangular by 32-blocks).
 #pragma unroll
-            for (int i = 0; i < 4; ++i) eye[i] = (4 * g4 + i == n) ? 1.f : 0.f;
-            const bf16x4_t a = to_bf4(adiag), at = to_bf4(adiagT);
-            const f32x4_t a2 = mma16(at, a, zero4());
-            const f32x4_t a2t = mma16(a, at, zero4());
-            const bf16x4_t a2b = to_bf4(a2), a2tb = to_bf4(a2t);
-            const f32x4_t a4 = mma16(a2tb, a2b, zero4());
-            const f32x4_t a4t = mma16(a2b, a2tb, zero4());
-            const bf16x4_t a4b = to_bf4(a4), a4tb = to_bf4(a4t);
-            const f32x4_t a8 = mma16(a4tb, a4b, zero4());
-            const bf16x4_t x1t = to_bf4(eye - adiagT), y1 = to_bf4(eye + a2);
-            const f32x4_t b1t = mma16(y1, x1t, zero4());         // ((I - A)(I + A^2))^T
-            const bf16x4_t b1tb = to_bf4(b1t), y2 = to_bf4(eye + a4);
-            const f32x4_t b2t = mma16(y2, b1tb, zero4());        // ((I-A)(I+A^2)(I+A^4))^T
-            const bf16x4_t b2tb = to_bf4(b2t), y3 = to_bf4(eye + a8);
-            TD[w * 64 + lane] = mma16(y3, b2tb, zero4());        // lay(T_ww^T)
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int k2 = 0; k2 < 2 * tb + 2; ++k2)
+                    ot[tb] = mfma32(vna[k2], ld8(set, S_P + sw128(32 * tb + c32, 2 * k2 + hh)), ot[tb]);
+            // Outputs: lane holds 4 consecutive columns of one token per group.
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const int r = 32 * tb + c32;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    bf16x4_t o;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = (__bf16)ot[tb][4 * m + i];
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, o), orsrc,
+                                                          ((t0 + r) * DV + 32 * cw + 8 * m + 4 * hh) * 2, 0, 0);
+                }
             }
-            __syncthreads();
-            {
-            if (c + 1 < nchunks) stage();
-            if (c + 2 < nchunks) issue(c + 2);
-            }
-            __syncthreads();
-            {
-            // S <- exp(gamC) S + (decayed K)^T Vnew, key rows [32w, 32w+32).
-            const float egC = __expf(gamC);
+            // S <- exp(gamma_C) S0 + K^T (decayed Vnew).
+            const float egC = vec[128];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int f = 0; f < 4; ++f) st[f] *= egC;
 #pragma unroll
-                for (int ct = 0; ct < DVT / 16; ++ct) st[rt][ct] *= egC;
+            for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int s = 0; s < C / 32; ++s) {
-                bf16x8_t ak[2], bv[DVT / 16];
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-                    ak[rt] = *reinterpret_cast<const bf16x8_t *>(KTs + (32 * w + 16 * rt + n) * LDC + 32 * s + 8 * g4);
-#pragma unroll
-                for (int ct = 0; ct < DVT / 16; ++ct)
-                    bv[ct] = *reinterpret_cast<const bf16x8_t *>(VNTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < DVT / 16; ++ct) st[rt][ct] = mma32(ak[rt], bv[ct], st[rt][ct]);
-            }
-            write_st();
-            }
-            __syncthreads();
+                for (int k2 = 0; k2 < 4; ++k2)
+                    st[f] = mfma32(ld8(set, S_KT + sw128(32 * f + c32, 2 * k2 + hh)), vnb[k2], st[f]);
+            lds_barrier();
         }
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                fb[(size_t)(32 * f + drow(q, hh)) * DV + 32 * cw + c32] = from_f32<bf16_t>(st[f][q]);
     } else {
-        f32x4_t yq[DVT / 16];   // exp(gam) Q S for the output
-        for (int c = 0; c < nchunks; ++c) {
-        const int t0 = c * C;
-        const int nval = min(C, L - t0);
+        // ------------------------------- prep ------------------------------
+        // Identity as a right operand in k-order (exact transposes).
+        bf16x8_t eye[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
 
-        // ---- in-chunk cumulative log decay (every wave, lane t = token t) ----
-        float gam = gs[lane];
+        // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
+        // waves 0-1 2 x 32 bytes of V and one beta (wave 0) or g (wave 1), so
+        // the two waves that invert the diagonal blocks carry the fewest.
+        // Rows past the valid length load as zeros (identity steps).
+        u32x4_t ra[8];
+        uint32_t rb = 0, rg = 0;
+        const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
+        auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
+            constexpr int W = decltype(R)::value;
+            const int t0 = cn * C, nv = min(C, L - t0);
+            if constexpr (W >= 2) {
 #pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const float y = __shfl_up(gam, d);
-            if (lane >= d) gam += y;
-        }
-        const float gamC = __shfl(gam, 63);
-        const float bet = betas[lane];
+                for (int m = 0; m < 2; ++m) {
+                    const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
+                    const u32x4_t z = {0u, 0u, 0u, 0u};
+                    ra[2 * m] = z; ra[2 * m + 1] = z; ra[4 + 2 * m] = z; ra[5 + 2 * m] = z;
+                    if (row < nv) {
+                        const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(kb + (size_t)(t0 + row) * DK + 16 * grp);
+                        const u32x4_t *qp = reinterpret_cast<const u32x4_t *>(qb + (size_t)(t0 + row) * DK + 16 * grp);
+                        ra[2 * m] = kp[0]; ra[2 * m + 1] = kp[1];
+                        ra[4 + 2 * m] = qp[0]; ra[5 + 2 * m] = qp[1];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
+                    const u32x4_t z = {0u, 0u, 0u, 0u};
+                    ra[2 * m] = z; ra[2 * m + 1] = z;
+                    if (row < nv) {
+                        const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vb + (size_t)(t0 + row) * DV + 16 * grp);
+                        ra[2 * m] = vp[0]; ra[2 * m + 1] = vp[1];
+                    }
+                }
+                if constexpr (W == 1) {
+                    rb = 0; rg = 0;
+                    if (lane < nv) {
+                        rb = betab[t0 + lane];
+                        if (gb) rg = reinterpret_cast<const uint32_t *>(gb)[t0 + lane];
+                    }
+                }
+            }
+        };
+        // 16 consecutive elements (pieces a, b) into k-order: slots 0-3 and
+        // 12-15 stay, slots 4-7 take elements 8-11, slots 8-11 elements 4-7.
+        auto korder_lo = [](u32x4_t a, u32x4_t b) { return u32x4_t{a.x, a.y, b.x, b.y}; };
+        auto korder_hi = [](u32x4_t a, u32x4_t b) { return u32x4_t{a.z, a.w, b.z, b.w}; };
+        float *bg = reinterpret_cast<float *>(smem + P_BG);
 
-            {
-            // K S and Q S for row block w; X = beta (V - exp(gam) K S).
-            float brr[4], egr[4];
+        auto prep = [&](auto R, int cn) __attribute__((always_inline)) {
+            constexpr int W = decltype(R)::value;
+            unsigned char *set = smem + (cn & 1) * SET_BYTES;
+            const uint32_t ncall = (uint32_t)cn + 1u;
+
+            // ---- stage chunk cn (K rows into the W slot, V rows into the U slot) ----
+            if constexpr (W >= 2) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * w + 4 * g4 + i;
-                brr[i] = __shfl(bet, r);
-                egr[i] = __expf(__shfl(gam, r));
-            }
-            f32x4_t yk[DVT / 16];
+                for (int m = 0; m < 2; ++m) {
+                    const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
+                    *reinterpret_cast<u32x4_t *>(set + S_W + sw256(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_W + sw256(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp)) = korder_lo(ra[4 + 2 * m], ra[5 + 2 * m]);
+                    *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp + 1)) = korder_hi(ra[4 + 2 * m], ra[5 + 2 * m]);
+                }
+            } else {
 #pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct) { yk[ct] = zero4(); yq[ct] = zero4(); }
-#pragma unroll
-            for (int s = 0; s < DK / 32; ++s) {
-                const bf16x8_t ak = *reinterpret_cast<const bf16x8_t *>(Ks + (16 * w + n) * LDK + 32 * s + 8 * g4);
-                const bf16x8_t aq = *reinterpret_cast<const bf16x8_t *>(Qs + (16 * w + n) * LDK + 32 * s + 8 * g4);
-#pragma unroll
-                for (int ct = 0; ct < DVT / 16; ++ct) {
-                    const bf16x8_t bs = *reinterpret_cast<const bf16x8_t *>(STs + (16 * ct + n) * LDK + 32 * s + 8 * g4);
-                    yk[ct] = mma32(ak, bs, yk[ct]);
-                    yq[ct] = mma32(aq, bs, yq[ct]);
+                for (int m = 0; m < 2; ++m) {
+                    const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
+                    *reinterpret_cast<u32x4_t *>(set + S_U + sw128(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_U + sw128(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                }
+                if constexpr (W == 1) {
+                    // Per-token factors of chunk cn (lane t = token t): gamma is the
+                    // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
+                    const int nv = min(C, L - cn * C);
+                    const float beta = __uint_as_float(rb << 16);
+                    const float gam2 = wave_prefix_sum(__uint_as_float(rg)) * 1.44269504088896340736f;
+                    const float gamC2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam2), 63));
+                    const float eg = __builtin_amdgcn_exp2f(gam2);
+                    bg[lane] = beta;
+                    bg[64 + lane] = gam2;
+                    bg[128 + lane] = beta * eg;
+                    float *vec = reinterpret_cast<float *>(set + S_VEC);
+                    vec[lane] = lane < nv ? p.scale * eg : 0.f;
+                    vec[64 + lane] = __builtin_amdgcn_exp2f(gamC2 - gam2);
+                    if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
                 }
             }
+            if (cn + 1 < nchunks) issue(R, cn + 1);
+            arrive(flags + 0, lane);
+            wait_for(flags + 0, 6u * ncall);
+
+            // beta, gamma log2(e) and beta exp(gamma) of the rows a lane holds in
+            // a result tile: rows 8m + 4hh + i of the 32-row block starting at r0.
+            const float *gv = bg + 64, *fv = bg + 128;
+            auto rows4 = [&](const float *v, int r0, float *o) __attribute__((always_inline)) {
 #pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct) {
-                f32x4_t x;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * w + 4 * g4 + i;
-                    const float vv = (float)Vs[r * LDC + 16 * ct + n];
-                    x[i] = brr[i] * (vv - egr[i] * yk[ct][i]);
-                    yq[ct][i] *= egr[i];
+                for (int m = 0; m < 4; ++m) {
+                    const float4 x = *reinterpret_cast<const float4 *>(v + r0 + 8 * m + 4 * hh);
+                    o[4 * m] = x.x; o[4 * m + 1] = x.y; o[4 * m + 2] = x.z; o[4 * m + 3] = x.w;
                 }
-                *reinterpret_cast<bf16x4_t *>(XTs + (16 * ct + n) * LDC + 16 * w + 4 * g4) = to_bf4(x);
-            }
-            // decayed K^T: KT[dk][t] = exp(gamC - gam_t) K[t][dk] (256 chain threads, 512 items)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int id = (tid - 256) + 256 * m;   // 32 token pairs x 16 key groups
-                const int tp = (id & 31) * 2, dg = (id >> 5) * 8;
-                const float e0 = __expf(gamC - __shfl(gam, tp));
-                const float e1 = __expf(gamC - __shfl(gam, tp + 1));
-                const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t *>(Ks + tp * LDK + dg);
-                const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t *>(Ks + (tp + 1) * LDK + dg);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    __bf16 pr[2];
-                    pr[0] = (__bf16)((float)k0[i] * e0);
-                    pr[1] = (__bf16)((float)k1[i] * e1);
-                    *reinterpret_cast<uint32_t *>(KTs + (dg + i) * LDC + tp) = *reinterpret_cast<uint32_t *>(pr);
-                }
-            }
-            }
-            __syncthreads();
-            {
-            // (I + A) Vnew = X for column tile ct = w, row block by row block:
-            // Vnew_i = T_ii (X_i - sum_{j<i} A_ij Vnew_j). Left-hand operand
-            // of -A_ij: lane holds -A[16i + n][16j + 4*g4 .. +3].
-            const int ct = w;
-            auto naop = [&](int i, int j) __attribute__((always_inline)) {
-                return to_bf4(-*reinterpret_cast<const f32x4_t *>(As + (16 * i + n) * LDA + 16 * j + 4 * g4));
             };
-            bf16x4_t vnb[4];
+
+            // Transposes by a product with the identity: job j < 8 is the
+            // K block (tokens 32(j&1), features 32(j>>1)), else the V block
+            // (tokens 32(j&1), columns 32((j-8)>>1)).
+            auto transpose = [&](int j) __attribute__((always_inline)) {
+                const int tb = j & 1, xb = (j & 7) >> 1;
+                f32x16_t d = zero16();
+                if (j < 8) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bf16x4_t xb = *reinterpret_cast<const bf16x4_t *>(XTs + (16 * ct + n) * LDC + 16 * i + 4 * g4);
-                f32x4_t acc;
+                    for (int s = 0; s < 2; ++s) d = mfma32(ld8(set, S_W + sw256(32 * tb + c32, 2 * (2 * xb + s) + hh)), eye[s], d);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = (float)xb[e];
+                    for (int s = 0; s < 2; ++s) st8(set, S_KT + sw128(32 * xb + c32, 2 * (2 * tb + s) + hh), op8(d, s));
+                } else {
 #pragma unroll
-                for (int j = 0; j < i; ++j) acc = mma16(naop(i, j), vnb[j], acc);
-                const f32x4_t vn = mma16(to_bf4(TD[i * 64 + lane]), to_bf4(acc), zero4());
-                vnb[i] = to_bf4(vn);
-                *reinterpret_cast<bf16x4_t *>(VNTs + (16 * ct + n) * LDC + 16 * i + 4 * g4) = vnb[i];
+                    for (int s = 0; s < 2; ++s) d = mfma32(ld8(set, S_U + sw128(32 * tb + c32, 2 * (2 * xb + s) + hh)), eye[s], d);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) st8(smem, P_VT + sw128(32 * xb + c32, 2 * (2 * tb + s) + hh), op8(d, s));
+                }
+            };
+
+            if constexpr (W < 2) {
+                // Diagonal block d of A and its inverse.
+                constexpr int d = W;
+                f32x16_t G = zero16();
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    const bf16x8_t a = ld8(set, S_W + sw256(32 * d + c32, 2 * ks + hh));
+                    G = mfma32(a, a, G);
+                }
+                float br[16], gr[16];
+                rows4(bg, 32 * d, br);
+                rows4(gv, 32 * d, gr);
+                const float bc = bg[32 * d + c32], gc = gv[32 * d + c32];
+                // N = D(-A_dd), Nt = D(-A_dd^T), R = D((I - A_dd)^T). At each
+                // position only one of A_dd, A_dd^T can be nonzero (G = K K^T is
+                // symmetric), so one exponential serves both.
+                f32x16_t N, Nt, R;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int rl = drow(q, hh);
+                    const bool below = c32 < rl;
+                    const float dg = gr[q] - gc;
+                    const float a = -__builtin_amdgcn_exp2f(below ? dg : -dg) * (below ? br[q] : bc) * G[q];
+                    N[q] = below ? a : 0.f;
+                    Nt[q] = rl < c32 ? a : 0.f;
+                    R[q] = rl == c32 ? 1.f : Nt[q];
+                }
+                // R_{k+1}^T = R_k^T + (N^(2^k))^T R_k^T, powers by squaring.
+                f32x16_t M = prod(Nt, N, zero16()), Mt = prod(N, Nt, zero16());   // N^2
+                R = prod(M, R, R);
+                f32x16_t M2 = prod(Mt, M, zero16()), M2t = prod(M, Mt, zero16());  // N^4
+                R = prod(M2, R, R);
+                M = prod(M2t, M2, zero16()); Mt = prod(M2, M2t, zero16());       // N^8
+                R = prod(M, R, R);
+                M2 = prod(Mt, M, zero16());                                       // N^16
+                R = prod(M2, R, R);                                               // D(T_dd^T)
+                // T' = T diag(beta exp(gamma)), Tb = T diag(beta), block (d, d).
+                float fp[16];
+                rows4(fv, 32 * d, fp);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    bf16x8_t tp, tq;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        tp[e] = (__bf16)(R[8 * s + e] * fp[8 * s + e]);
+                        tq[e] = (__bf16)(R[8 * s + e] * br[8 * s + e]);
+                    }
+                    st8(smem, P_TP + sw128(32 * d + c32, 2 * (2 * d + s) + hh), tp);
+                    st8(smem, P_TB + sw128(32 * d + c32, 2 * (2 * d + s) + hh), tq);
+                }
+                if constexpr (d == 1) {
+                    // Z = -(T_11 A_10)^T = -A_10^T T_11^T.
+                    wait_for(flags + 1, ncall);
+                    const bf16x8_t a0 = ld8(smem, P_A10 + lane * 16), a1 = ld8(smem, P_A10 + 1024 + lane * 16);
+                    f32x16_t Z = mfma32(a0, op8(R, 0), zero16());
+                    Z = mfma32(a1, op8(R, 1), Z);
+                    Z = -Z;
+                    st8(smem, P_Z + lane * 16, op8(Z, 0));
+                    st8(smem, P_Z + 1024 + lane * 16, op8(Z, 1));
+                    arrive(flags + 2, lane);
+                } else {
+                    // T_10^T = T_00^T Z; D(T_00) from D(T_00^T) and the identity.
+                    f32x16_t T0 = mfma32(op8(R, 0), eye[0], zero16());
+                    T0 = mfma32(op8(R, 1), eye[1], T0);
+                    wait_for(flags + 2, ncall);
+                    const bf16x8_t z0 = ld8(smem, P_Z + lane * 16), z1 = ld8(smem, P_Z + 1024 + lane * 16);
+                    f32x16_t T10 = mfma32(op8(T0, 0), z0, zero16());
+                    T10 = mfma32(op8(T0, 1), z1, T10);
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        bf16x8_t tp, tq;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            tp[e] = (__bf16)(T10[8 * s + e] * fp[8 * s + e]);
+                            tq[e] = (__bf16)(T10[8 * s + e] * br[8 * s + e]);
+                        }
+                        st8(smem, P_TP + sw128(32 + c32, 2 * s + hh), tp);
+                        st8(smem, P_TB + sw128(32 + c32, 2 * s + hh), tq);
+                    }
+                }
+            } else if constexpr (W == 2) {
+                // A_10: rows 32-63 of A against columns 0-31 (no mask needed).
+                f32x16_t G = zero16();
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks)
+                    G = mfma32(ld8(set, S_W + sw256(32 + c32, 2 * ks + hh)), ld8(set, S_W + sw256(c32, 2 * ks + hh)), G);
+                const float gi = gv[c32];
+                float br[16], gr[16];
+                rows4(bg, 32, br);
+                rows4(gv, 32, gr);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) G[q] *= br[q] * __builtin_amdgcn_exp2f(gr[q] - gi);
+                st8(smem, P_A10 + lane * 16, op8(G, 0));
+                st8(smem, P_A10 + 1024 + lane * 16, op8(G, 1));
+                arrive(flags + 1, lane);
+            } else {
+                // P block (tokens r in block rbq, keys i in block ibq), written as rows r.
+                constexpr int rbq = W == 3 ? 0 : 1, ibq = W == 5 ? 1 : 0;
+                f32x16_t G = zero16();
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks)
+                    G = mfma32(ld8(set, S_W + sw256(32 * ibq + c32, 2 * ks + hh)),
+                               ld8(set, S_Q + sw256(32 * rbq + c32, 2 * ks + hh)), G);
+                const int r = 32 * rbq + c32;
+                const float gq = gv[r];
+                float gi[16];
+                rows4(gv, 32 * ibq, gi);
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int i = 32 * ibq + drow(q, hh);
+                    G[q] = i <= r ? p.scale * __builtin_amdgcn_exp2f(gq - gi[q]) * G[q] : 0.f;
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
             }
+            if constexpr (W >= 2) {
+#pragma unroll
+                for (int j = 0; j < 3; ++j) transpose(3 * (W - 2) + j);
             }
-            __syncthreads();
-            {
-            // O = scale (exp(gam) Q S + P Vnew) for row block w, staged through
-            // this wave's part of the X^T buffer as rows, then stored 16 bytes
-            // at a time.
-            const int ks = w >= 2 ? 2 : 1;
-            f32x4_t o[DVT / 16];
+            // T', Tb, K^T, V^T complete; K and V rows no longer read.
+            arrive(flags + 3, lane);
+            wait_for(flags + 3, 6u * ncall);
+
+            if constexpr (W < 4) {
+                // -W^T = -(K^T T'^T), features [32W, 32W + 32), written as -W rows.
+                constexpr int fbk = W;
+                bf16x8_t ak[4];
 #pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct) o[ct] = yq[ct];
-            for (int s = 0; s < ks; ++s) {
-                const bf16x8_t ap = *reinterpret_cast<const bf16x8_t *>(Ps + (16 * w + n) * LDC + 32 * s + 8 * g4);
+                for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ld8(set, S_KT + sw128(32 * fbk + c32, 2 * k2 + hh));
 #pragma unroll
-                for (int ct = 0; ct < DVT / 16; ++ct) {
-                    const bf16x8_t bv = *reinterpret_cast<const bf16x8_t *>(VNTs + (16 * ct + n) * LDC + 32 * s + 8 * g4);
-                    o[ct] = mma32(ap, bv, o[ct]);
+                for (int rb = 0; rb < 2; ++rb) {
+                    f32x16_t d = zero16();
+#pragma unroll
+                    for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
+                        d = mfma32(ak[k2], ld8(smem, P_TP + sw128(32 * rb + c32, 2 * k2 + hh)), d);
+                    d = -d;
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8(d, s));
+                }
+            } else {
+                // U = Tb V for value columns [32vb, 32vb + 32), kept in result order.
+                constexpr int vbk = W - 4;
+                bf16x8_t bv[4];
+#pragma unroll
+                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ld8(smem, P_VT + sw128(32 * vbk + c32, 2 * k2 + hh));
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    f32x16_t d = zero16();
+#pragma unroll
+                    for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
+                        d = mfma32(ld8(smem, P_TB + sw128(32 * rb + c32, 2 * k2 + hh)), bv[k2], d);
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) st8(set, S_U + ((vbk * 2 + rb) * 2 + q) * 1024 + lane * 16, op8(d, q));
                 }
             }
-            __bf16 *Os = XTs;   // rows [16w, 16w + 16) of a [C][LDC] row-major view
-#pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * w + 4 * g4 + i;
-                    Os[r * LDC + 16 * ct + n] = (__bf16)(r < nval ? p.scale * o[ct][i] : 0.f);
-                }
-            __builtin_amdgcn_wave_barrier();
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int id = lane + 64 * m;             // 16 rows x 8 pieces
-                const int r = 16 * w + (id >> 3), cv = (id & 7) * 8;
-                if (t0 + r < S)
-                    *reinterpret_cast<uint4 *>(ob + (size_t)(t0 + r) * DV + cv) =
-                        *reinterpret_cast<const uint4 *>(Os + r * LDC + cv);
+        };
+
+        // Each role runs its own copy of the loop, so that it keeps only its
+        // own addresses and values live.
+        auto run = [&](auto R) __attribute__((always_inline)) {
+            if (nchunks > 0) {
+                issue(R, 0);
+                prep(R, 0);
+                lds_barrier();
             }
+            for (int c = 0; c < nchunks; ++c) {
+                if (c + 1 < nchunks) prep(R, c + 1);
+                lds_barrier();
             }
-            __syncthreads();
+        };
+        switch (wv) {
+        case 0: run(std::integral_constant<int, 0>{}); break;
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        default: run(std::integral_constant<int, 5>{}); break;
         }
     }
 
-    // Final state of this tile, then zeros for every output row past the
-    // last processed chunk.
-    if (prep) {
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < DVT / 16; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int dk = 32 * w + 16 * rt + 4 * g4 + i;
-                    fb[(size_t)dk * DV + 16 * ct + n] = from_f32<bf16_t>(st[rt][ct][i]);
-                }
-    }
+    // Zeros for every output row past the last processed chunk.
     const int tz = nchunks * C;
     for (int id = tid; id < (S - tz) * (DVT / 8); id += NTHR) {
         const int row = tz + id / (DVT / 8), cv = (id % (DVT / 8)) * 8;
