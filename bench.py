@@ -12,9 +12,11 @@ exceeds the 256 MB last-level cache. Kernel time comes from HIP events
 recorded on the stream the kernels are launched on. Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -42,6 +44,39 @@ def dev(a):
 
 def esize(dtype):
     return 2 if dtype == "bf16" else 4
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE), from profiles/
+# ---------------------------------------------------------------------------
+CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_amd", "csrc")
+KERNEL_SOURCES = {
+    "decode": ["gdr_decode.hip", "gdr_common.h"],
+    "chunk": ["gdr_chunk.hip", "gdr_common.h"],
+}
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(profile, kind):
+    """HBM bytes per launch recorded in a profiles/ summary, or None when the
+    summary is missing or was taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", profile)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel source sha256: `([0-9a-f]{64})`", text)
+    m_bytes = re.search(r"traffic bytes per launch: `(\d+)`", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kind):
+        return None
+    return int(m_bytes.group(1))
 
 
 # ---------------------------------------------------------------------------
@@ -273,7 +308,8 @@ def main():
             "state_frac_hbm": state_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "roofline": {"kernel": "decode_kernel<bf16,128,128>", "bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_launch": bytes_call},
+                         "traffic": measured_traffic("decode_kernel_decode_step.txt", "decode"),
+                         "algorithmic_bytes_per_launch": bytes_call},
             "wall_s_timed": wall,
         })
         del keep, calls
@@ -293,8 +329,9 @@ def main():
                                       "lengths and accepted counts U{1..4}, 256-slot pool",
                           "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
                           "state_GBps": state_b / (ms * 1e-3) / 1e9,
-                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                          "roofline": {"kernel": "decode_kernel<bf16,128,128>", "bound": "hbm", "achieved": gbs,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                       "traffic": measured_traffic("decode_kernel_speculative_decode.txt", "decode"),
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls
         torch.cuda.empty_cache()
@@ -302,11 +339,12 @@ def main():
     prefill_sets = []
     if args.only in (None, "prefill"):
         prefill_sets.append(("chunked prefill", 4, "B=4 S=4096 Nk=16 Nv=32 Dk=Dv=128 bf16, g, initial state, C=64",
-                             [(0, 0), (1, 9), (2, 18), (3, 27)]))
+                             [(0, 0), (1, 9), (2, 18), (3, 27)], "chunk_mfma_kernel_chunked_prefill.txt"))
     if args.varlen or args.only == "varlen":
         prefill_sets.append(("varlen prefill", 5, "B=16 S=16384 (lengths U{256..16384}) Nk=16 Nv=64 Dk=Dv=128 "
-                             "bf16, no decay, zero initial state, C=64", [(0, 0), (5, 40)]))
-    for name, cid, desc, units in prefill_sets:
+                             "bf16, no decay, zero initial state, C=64", [(0, 0), (5, 40)],
+                             "chunk_mfma_kernel_varlen_prefill.txt"))
+    for name, cid, desc, units, profile in prefill_sets:
         log(f"{name}: generating inputs")
         c = synth.config(cid)
         bytes_call, flops, tok = prefill_work(c)
@@ -321,7 +359,7 @@ def main():
                  "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
                  "roofline": {"kernel": "chunk_mfma_kernel", "bound": "mfma", "achieved": tf,
                               "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
-                              "traffic": None, "algorithmic_flops_per_launch": flops,
+                              "traffic": measured_traffic(profile, "chunk"), "algorithmic_flops_per_launch": flops,
                               "algorithmic_bytes_per_launch": bytes_call}}
         del keep, calls
         torch.cuda.empty_cache()
