@@ -378,46 +378,46 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             for (int e = 0; e < 8; ++e)
                 eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
 
+        // Inputs are read through buffer resources bounded by the sequence's
+        // valid length: rows past it come back as zeros from the hardware
+        // bounds check (identity steps). Loads need no branch, and are issued
+        // even past the last chunk, so the loaded registers never meet control
+        // flow that would make the compiler wait for them on the spot.
+        const int Lk = L * DK * 2, Lv = (L * DV - col0) * 2;
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, Lk, 0x00020000);
+        const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void *)qb, (short)0, Lk, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, Lv, 0x00020000);
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc((void *)betab, (short)0, L * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void *)gb, (short)0, gb ? L * 4 : 0, 0x00020000);
         // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
-        // waves 0-1 2 x 32 bytes of V and one beta (wave 0) or g (wave 1), so
-        // the two waves that invert the diagonal blocks carry the fewest.
-        // Rows past the valid length load as zeros (identity steps).
+        // waves 0-1 2 x 32 bytes of V, and wave 1 one beta and one g.
         u32x4_t ra[8];
         uint32_t rb = 0, rg = 0;
         const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
         auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
             constexpr int W = decltype(R)::value;
-            const int t0 = cn * C, nv = min(C, L - t0);
+            const int t0 = cn * C;
             if constexpr (W >= 2) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
-                    const u32x4_t z = {0u, 0u, 0u, 0u};
-                    ra[2 * m] = z; ra[2 * m + 1] = z; ra[4 + 2 * m] = z; ra[5 + 2 * m] = z;
-                    if (row < nv) {
-                        const u32x4_t *kp = reinterpret_cast<const u32x4_t *>(kb + (size_t)(t0 + row) * DK + 16 * grp);
-                        const u32x4_t *qp = reinterpret_cast<const u32x4_t *>(qb + (size_t)(t0 + row) * DK + 16 * grp);
-                        ra[2 * m] = kp[0]; ra[2 * m + 1] = kp[1];
-                        ra[4 + 2 * m] = qp[0]; ra[5 + 2 * m] = qp[1];
-                    }
+                    const int off = ((t0 + row) * DK + 16 * grp) * 2;
+                    ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                    ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
+                    ra[4 + 2 * m] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+                    ra[5 + 2 * m] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0);
                 }
             } else {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
-                    const u32x4_t z = {0u, 0u, 0u, 0u};
-                    ra[2 * m] = z; ra[2 * m + 1] = z;
-                    if (row < nv) {
-                        const u32x4_t *vp = reinterpret_cast<const u32x4_t *>(vb + (size_t)(t0 + row) * DV + 16 * grp);
-                        ra[2 * m] = vp[0]; ra[2 * m + 1] = vp[1];
-                    }
+                    const int off = ((t0 + row) * DV + 16 * grp) * 2;
+                    ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+                    ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16, 0, 0);
                 }
                 if constexpr (W == 1) {
-                    rb = 0; rg = 0;
-                    if (lane < nv) {
-                        rb = betab[t0 + lane];
-                        if (gb) rg = reinterpret_cast<const uint32_t *>(gb)[t0 + lane];
-                    }
+                    rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
+                    rg = __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
                 }
             }
         };
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
                 }
             }
-            if (cn + 1 < nchunks) issue(R, cn + 1);
+            issue(R, cn + 1);
             arrive(flags + 0, lane);
             wait_for(flags + 0, 6u * ncall);
 
@@ -664,10 +664,11 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 issue(R, 0);
                 prep(R, 0);
                 lds_barrier();
-            }
-            for (int c = 0; c < nchunks; ++c) {
-                if (c + 1 < nchunks) prep(R, c + 1);
-                lds_barrier();
+                for (int c = 0; c + 1 < nchunks; ++c) {
+                    prep(R, c + 1);
+                    lds_barrier();
+                }
+                lds_barrier();   // the chain's last chunk
             }
         };
         switch (wv) {
