@@ -186,6 +186,232 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
         for (int t = L; t < S; ++t) VecIO<T, VEC>::store(out + (vh * S + t) * DV + col, zero);
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Decode step with one token per sequence (S = 1), bf16, Dk = Dv = 128: the
+// state stream as a persistent, software-pipelined walk. Each wavefront owns
+// the 32-column tiles w, w + G, w + 2G, ... of all (b, h) states and keeps
+// the loads of the next tile in flight while it updates and stores the
+// current one (two register sets, alternating). Every load goes through a
+// buffer resource whose size is zero when the tile has nothing to read (a
+// skipped sequence, or past the last tile), so loads never sit under a branch
+// and never make the wave wait before their data is used.
+//
+// With one token the output needs no pass over the updated state:
+//   S' = D S + k delta^T,  D = diag(exp(g) exp(gk_i)),  delta = beta (v - S^T D k)
+//   o  = scale S'^T q = scale (S^T (D q) + delta (k . q))
+// so S^T (D k) and S^T (D q) come from one pass over S and the store of S'
+// follows the update directly.
+namespace s1 {
+constexpr int DK = 128, DV = 128, TV = 32, VEC = 8;
+constexpr int CG = TV / VEC;    // 4 column groups of 8 columns
+constexpr int RG = 64 / CG;     // 16 lanes across the rows
+constexpr int RPL = DK / RG;    // 8 rows per lane
+constexpr int NT = DV / TV;     // 4 tiles per head
+constexpr int WPB = 4;          // wavefronts per workgroup
+constexpr int WAVES = 2048;     // persistent wavefronts (8 per CU)
+}  // namespace s1
+
+// Per-tile values read through the scalar cache, one half-step before use.
+struct S1Scal { int32_t len, nacc, idx, beta2, g; };
+// Per-tile values after resolution, and the vector registers of its loads.
+struct S1Tile { int b, h, ct, r; float beta, g; };
+struct S1Regs {
+    u32x4_t st[s1::RPL];   // state rows, 8 bf16 columns each
+    u32x4_t k, q, v;       // k, q rows of this lane; v columns of this lane (bf16)
+    u32x4_t gk[2];         // per-key gate of this lane's rows (f32)
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *p, int bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
+}
+
+template <bool GK>
+__global__ __launch_bounds__(256) void decode_s1_kernel(DecodeParams p, int ntiles)
+{
+    using namespace s1;
+    const int lane = threadIdx.x & 63;
+    const int w = uniform(blockIdx.x * WPB + (threadIdx.x >> 6));
+    const int G = uniform(gridDim.x * WPB);
+    const int Nv = p.Nv, rep = p.Nv / p.Nk;
+    const int rg = lane % RG, cg = lane / RG;
+    const int row0 = rg * RPL;
+
+    const bf16_t *q = static_cast<const bf16_t *>(p.q);
+    const bf16_t *k = static_cast<const bf16_t *>(p.k);
+    const bf16_t *v = static_cast<const bf16_t *>(p.v);
+    bf16_t *pool = static_cast<bf16_t *>(p.pool);
+    bf16_t *out = static_cast<bf16_t *>(p.out);
+    // Optional inputs are read from a valid stand-in address and discarded,
+    // so no load sits under a branch.
+    const int32_t *nacc_src = p.nacc ? p.nacc : p.lens;
+    const int32_t *g_src = p.g ? reinterpret_cast<const int32_t *>(p.g) : p.lens;
+    const int32_t *beta_src = static_cast<const int32_t *>(p.beta);
+
+    auto coords = [&](int tile, int &b, int &h, int &ct) __attribute__((always_inline)) {
+        const int tt = tile < ntiles ? tile : 0;
+        ct = tt % NT;
+        const int bh = tt / NT;
+        h = bh % Nv;
+        b = bh / Nv;
+    };
+    // Issues the scalar loads of a tile (they complete while the wave works).
+    auto scal = [&](int tile) __attribute__((always_inline)) {
+        int b, h, ct;
+        coords(tile, b, h, ct);
+        const size_t vh = (size_t)b * Nv + h;
+        S1Scal c;
+        c.len = ld_const(p.lens, b);
+        c.nacc = ld_const(nacc_src, b);
+        c.idx = ld_const(p.idx, b);
+        c.beta2 = ld_const(beta_src, vh >> 1);
+        c.g = ld_const(g_src, p.g ? vh : 0);
+        return c;
+    };
+    // Resolves a tile from its scalars and issues its vector loads.
+    auto vec = [&](S1Regs &R, S1Tile &t, const S1Scal &c, int tile) __attribute__((always_inline)) {
+        coords(tile, t.b, t.h, t.ct);
+        const size_t vh = (size_t)t.b * Nv + t.h;
+        const int L = c.len < 0 ? 0 : (c.len > 1 ? 1 : c.len);
+        const int n = p.nacc ? c.nacc : L;
+        const int r = (tile < ntiles && L == 1 && n == 1) ? c.idx : -1;
+        t.r = (r >= 0 && r < p.slots) ? r : -1;
+        t.beta = __uint_as_float(((uint32_t)c.beta2 >> (16 * (int)(vh & 1))) << 16);
+        t.g = p.g ? __int_as_float(c.g) : 0.f;
+        const bool on = t.r >= 0;
+        const size_t qk = (size_t)t.b * p.Nk + t.h / rep;
+        const int col = t.ct * TV;
+        const auto srs = brsrc(pool + ((size_t)(on ? t.r : 0) * Nv + t.h) * DK * DV + col, on ? (DK * DV - col) * 2 : 0);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+            R.st[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * VEC) * 2, 0, 0);
+        const int tb = on ? DK * 2 : 0;
+        R.k = __builtin_amdgcn_raw_buffer_load_b128(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
+        R.q = __builtin_amdgcn_raw_buffer_load_b128(brsrc(q + qk * DK, tb), row0 * 2, 0, 0);
+        R.v = __builtin_amdgcn_raw_buffer_load_b128(brsrc(v + vh * DV + col, on ? (DV - col) * 2 : 0), cg * VEC * 2, 0, 0);
+        if constexpr (GK) {
+            const auto grs = brsrc(p.gk + vh * DK, on ? DK * 4 : 0);
+            R.gk[0] = __builtin_amdgcn_raw_buffer_load_b128(grs, row0 * 4, 0, 0);
+            R.gk[1] = __builtin_amdgcn_raw_buffer_load_b128(grs, row0 * 4 + 16, 0, 0);
+        }
+    };
+    // A tile that is skipped still waits for its (empty) loads, so that every
+    // path leaves the register set settled: otherwise the compiler has to wait
+    // for it where the paths meet, before the next prefetch is issued.
+    auto settle = [&](const S1Regs &R) __attribute__((always_inline)) {
+        uint32_t x = R.k.x ^ R.q.x ^ R.v.x;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) x ^= R.st[i].x ^ R.st[i].w;
+        if constexpr (GK) x ^= R.gk[0].x ^ R.gk[1].x;
+        asm volatile("" ::"v"(x));
+    };
+    auto compute = [&](const S1Regs &R, const S1Tile &t, int tile) __attribute__((always_inline)) {
+        if (tile >= ntiles) {
+            settle(R);
+            return;
+        }
+        const size_t vh = (size_t)t.b * Nv + t.h;
+        const int col = t.ct * TV + cg * VEC;
+        bf16_t *op = out + vh * DV + col;
+        if (t.r < 0) {
+            settle(R);
+            if (rg == 0) *reinterpret_cast<u32x4_t *>(op) = u32x4_t{0u, 0u, 0u, 0u};
+            return;
+        }
+        // D = exp(g) exp(gk_i)
+        const float a = __expf(t.g);
+        const uint32_t kw[4] = {R.k.x, R.k.y, R.k.z, R.k.w}, qw[4] = {R.q.x, R.q.y, R.q.z, R.q.w};
+        float dd[RPL];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) dd[i] = a;
+        if constexpr (GK) {
+            const uint32_t gw[8] = {R.gk[0].x, R.gk[0].y, R.gk[0].z, R.gk[0].w, R.gk[1].x, R.gk[1].y, R.gk[1].z, R.gk[1].w};
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) dd[i] = a * __expf(__uint_as_float(gw[i]));
+        }
+        float kr[RPL], dk[RPL], dq[RPL], kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const float ki = (i & 1) ? bf16_hi(kw[i >> 1]) : bf16_lo(kw[i >> 1]);
+            const float qi = (i & 1) ? bf16_hi(qw[i >> 1]) : bf16_lo(qw[i >> 1]);
+            kr[i] = ki;
+            dk[i] = dd[i] * ki;
+            dq[i] = dd[i] * qi;
+            kq = fmaf(ki, qi, kq);
+        }
+        // One pass over S: S^T (D k) and S^T (D q) for this lane's columns.
+        float st[RPL][VEC];
+        float kv[VEC], sq[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) { kv[c] = 0.f; sq[c] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const uint32_t sw[4] = {R.st[i].x, R.st[i].y, R.st[i].z, R.st[i].w};
+#pragma unroll
+            for (int c = 0; c < VEC; ++c) {
+                st[i][c] = (c & 1) ? bf16_hi(sw[c >> 1]) : bf16_lo(sw[c >> 1]);
+                kv[c] = fmaf(st[i][c], dk[i], kv[c]);
+                sq[c] = fmaf(st[i][c], dq[i], sq[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) { kv[c] = group_sum<RG>(kv[c]); sq[c] = group_sum<RG>(sq[c]); }
+        kq = group_sum<RG>(kq);
+        // delta, the updated state (stored at once), then the output.
+        const uint32_t vw[4] = {R.v.x, R.v.y, R.v.z, R.v.w};
+        float dl[VEC];
+#pragma unroll
+        for (int c = 0; c < VEC; ++c) dl[c] = t.beta * (((c & 1) ? bf16_hi(vw[c >> 1]) : bf16_lo(vw[c >> 1])) - kv[c]);
+        const auto srs = brsrc(pool + ((size_t)t.r * Nv + t.h) * DK * DV + t.ct * TV, (DK * DV - t.ct * TV) * 2);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            uint32_t ow[4];
+#pragma unroll
+            for (int c = 0; c < VEC; c += 2)
+                ow[c >> 1] = pack_bf16x2(fmaf(st[i][c], dd[i], kr[i] * dl[c]), fmaf(st[i][c + 1], dd[i], kr[i] * dl[c + 1]));
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, srs, ((row0 + i) * DV + cg * VEC) * 2, 0, 0);
+        }
+        if (rg == 0) {
+            uint32_t ow[4];
+#pragma unroll
+            for (int c = 0; c < VEC; c += 2)
+                ow[c >> 1] = pack_bf16x2(p.scale * fmaf(dl[c], kq, sq[c]), p.scale * fmaf(dl[c + 1], kq, sq[c + 1]));
+            *reinterpret_cast<u32x4_t *>(op) = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+        }
+    };
+
+    // Half-step for tile i (register set X): consume the scalars of tile
+    // i + G (issued one half-step earlier) and issue its vector loads into the
+    // other set; then issue the scalars of tile i + 2G; then compute tile i.
+    // The scheduling barriers keep each wait for scalars clear of the loads
+    // issued after it.
+    S1Regs A, B;
+    S1Tile tA, tB;
+    S1Scal cX, cY;
+    int tile = w;
+    cX = scal(tile);
+    vec(A, tA, cX, tile);
+    cY = scal(tile + G);
+    while (true) {
+        vec(B, tB, cY, tile + G);
+        __builtin_amdgcn_sched_barrier(0);
+        cX = scal(tile + 2 * G);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A, tA, tile);
+        tile += G;
+        if (tile >= ntiles) break;
+        vec(A, tA, cX, tile + G);
+        __builtin_amdgcn_sched_barrier(0);
+        cY = scal(tile + 2 * G);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(B, tB, tile);
+        tile += G;
+        if (tile >= ntiles) break;
+    }
+}
+
 // Tile and vector width per (type, Dk, Dv): 16-byte row segments where the
 // tile holds enough elements, a 32-column tile at most (measured fastest on
 // MI355X among 16/32/64-column tiles and 1-8 waves per workgroup).
@@ -226,6 +452,17 @@ static hipError_t launch_typed(int Dk, int Dv, const DecodeParams &p, hipStream_
 
 hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported)
 {
+    if (dtype == 1 && p.S == 1 && Dk == s1::DK && Dv == s1::DV) {
+        *supported = true;
+        const int ntiles = p.B * p.Nv * s1::NT;
+        const int waves = ntiles < s1::WAVES ? ntiles : s1::WAVES;
+        const dim3 grid((unsigned)((waves + s1::WPB - 1) / s1::WPB)), block(64 * s1::WPB);
+        DecodeParams pc = p;
+        int nt = ntiles;
+        void *args[] = {&pc, &nt};
+        const void *fn = p.gk ? (const void *)decode_s1_kernel<true> : (const void *)decode_s1_kernel<false>;
+        return hipLaunchKernel(fn, grid, block, args, 0, s);
+    }
     if (dtype == 1) return launch_typed<bf16_t>(Dk, Dv, p, s, supported);
     return launch_typed<float>(Dk, Dv, p, s, supported);
 }
