@@ -143,3 +143,45 @@ def test_decode_repeated_calls_advance_the_state():
         outs.append(to_f64(out)[:, :, 0])
     assert max_err(np.stack(outs, 2), o_ref) <= 2e-2
     assert max_err(to_f64(pool), p_ref) <= 2e-2
+
+
+# One-token steps of bf16 128 x 128 heads take the persistent, software-pipelined
+# kernel (each wavefront walks many 32-column tiles with two register sets);
+# these cases exercise its tile walk, its skipped tiles and both gate variants.
+@pytest.mark.parametrize("gk", [None, (-0.5, -0.001)])
+def test_single_token_skipped_tiles_and_gates(gk):
+    # lengths 0/1 and accepted counts 0..2 (0 and 2 are out of range for S = 1);
+    # some read slots out of range; NaN in every input of a sequence of length 0.
+    B, slots = 40, 64
+    rng = np.random.default_rng(4242)
+    lens = rng.integers(0, 2, B).astype(np.int32)
+    n_acc = rng.integers(0, 3, B).astype(np.int32)
+    idx = rng.permutation(slots)[:B].astype(np.int32)
+    idx[::7] = slots + 3
+    idx[3::11] = -2
+    c = synth.decode_case(B=B, Nk=4, Nv=16, S=1, Dk=128, Dv=128, slots=slots, gk=gk, lens=lens,
+                          n_acc=n_acc, idx=idx, base=4242, poison_pad=True)
+    say(f"single token: skipped {int((lens == 0).sum())} by length, gk={gk is not None}")
+    out, pool = run_decode(c)
+    assert bool(torch.isfinite(out.float()).all())
+    _check_decode(c, out, pool)
+
+
+def test_single_token_many_tiles_per_wave():
+    # 97 * 32 * 4 = 12416 tiles: about six per wavefront, with a ragged tail.
+    c = synth.decode_case(B=97, Nk=8, Nv=32, S=1, Dk=128, Dv=128, slots=128, base=4343)
+    out, pool = run_decode(c)
+    _check_decode(c, out, pool)
+
+
+def test_single_token_without_g_and_n_acc():
+    c = synth.decode_case(B=12, Nk=2, Nv=8, S=1, Dk=128, Dv=128, slots=16, gate=None, n_acc=None, base=4444)
+    out, pool = run_decode(c)
+    _check_decode(c, out, pool)
+
+
+def test_single_token_one_head():
+    # Four tiles in total: fewer tiles than wavefronts.
+    c = synth.decode_case(B=1, Nk=1, Nv=1, S=1, Dk=128, Dv=128, slots=3, base=4545)
+    out, pool = run_decode(c)
+    _check_decode(c, out, pool)
