@@ -306,7 +306,7 @@ def main():
                        "launch": args.launch},
             "state_GBps": state_b / (ms * 1e-3) / 1e9,
             "state_frac_hbm": state_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "roofline": {"kernel": "decode_kernel<bf16,128,128>", "bound": "hbm", "achieved": gbs,
+            "roofline": {"kernel": "decode_s1_kernel (one-token bf16 128x128)", "bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                          "traffic": measured_traffic("decode_kernel_decode_step.txt", "decode"),
                          "algorithmic_bytes_per_launch": bytes_call},
