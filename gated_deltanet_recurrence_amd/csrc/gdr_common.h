@@ -43,11 +43,13 @@ typedef uint16_t bf16_t;
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats narrowed by one v_cvt_pk_bf16_f32 (a in the low half).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
-    __bf16 x = (__bf16)a;
-    __bf16 y = (__bf16)b;
-    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -189,38 +189,50 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Decode step with one token per sequence (S = 1), bf16, Dk = Dv = 128: the
-// state stream as a persistent, software-pipelined walk. Each wavefront owns
-// the 32-column tiles w, w + G, w + 2G, ... of all (b, h) states and keeps
-// the loads of the next tile in flight while it updates and stores the
-// current one (two register sets, alternating). Every load goes through a
-// buffer resource whose size is zero when the tile has nothing to read (a
-// skipped sequence, or past the last tile), so loads never sit under a branch
-// and never make the wave wait before their data is used.
+// Decode step with one token per sequence (S = 1), bf16, Dk = Dv = 128.
+//
+// A workgroup of eight wavefronts updates one head at a time and walks the
+// heads g, g + G, g + 2G, ... (G workgroups, persistent). Wave j owns the
+// 16 rows [16j, 16j + 16) of the head's 128 x 128 state; lane l of it holds
+// columns 8 (l % 16) .. + 7 of the four consecutive rows 16j + 4 (l / 16) + i,
+// so each load or store instruction of the wave moves four whole 256-byte
+// rows and the wave as a whole a contiguous 4 KiB block. The column sums
+// S^T (D k) and S^T (D q) are reduced over the wave's four lane rows with the
+// cross-row lane swaps (v_permlane32_swap / v_permlane16_swap), then over the
+// eight waves through LDS with one barrier per head. All loads of the next
+// head (state, k, q, v, gk) are in flight while the current head is updated
+// and stored; its scalars are read one head earlier still. Every load goes
+// through a buffer resource whose size is zero when there is nothing to read,
+// so no load sits under a branch.
 //
 // With one token the output needs no pass over the updated state:
 //   S' = D S + k delta^T,  D = diag(exp(g) exp(gk_i)),  delta = beta (v - S^T D k)
 //   o  = scale S'^T q = scale (S^T (D q) + delta (k . q))
-// so S^T (D k) and S^T (D q) come from one pass over S and the store of S'
-// follows the update directly.
 namespace s1 {
-constexpr int DK = 128, DV = 128, TV = 32, VEC = 8;
-constexpr int CG = TV / VEC;    // 4 column groups of 8 columns
-constexpr int RG = 64 / CG;     // 16 lanes across the rows
-constexpr int RPL = DK / RG;    // 8 rows per lane
-constexpr int NT = DV / TV;     // 4 tiles per head
-constexpr int WPB = 4;          // wavefronts per workgroup
-constexpr int WAVES = 2048;     // persistent wavefronts (8 per CU)
+constexpr int DK = 128, DV = 128;
+constexpr int NW = 8;                 // waves per head (workgroup size 512)
+constexpr int RW = DK / NW;           // 16 rows per wave
+constexpr int NI = RW / 4;            // 4 rows per lane, one per instruction
+#ifndef GDR_S1_GROUPS
+#define GDR_S1_GROUPS 256
+#endif
+constexpr int GROUPS = GDR_S1_GROUPS; // persistent workgroups
+#ifndef GDR_S1_NB
+#define GDR_S1_NB 3
+#endif
+constexpr int NB = GDR_S1_NB;         // heads whose loads are in flight
 }  // namespace s1
 
-// Per-tile values read through the scalar cache, one half-step before use.
+// Scalars of a head, read through the scalar cache ahead of use.
 struct S1Scal { int32_t len, nacc, idx, beta2, g; };
-// Per-tile values after resolution, and the vector registers of its loads.
-struct S1Tile { int b, h, ct, r; float beta, g; };
-struct S1Regs {
-    u32x4_t st[s1::RPL];   // state rows, 8 bf16 columns each
-    u32x4_t k, q, v;       // k, q rows of this lane; v columns of this lane (bf16)
-    u32x4_t gk[2];         // per-key gate of this lane's rows (f32)
+// One head's loads and resolution (r < 0: nothing to do).
+struct S1Head {
+    int b, h, r;
+    float beta, g;
+    u32x4_t st[s1::NI];   // 8 bf16 columns of each of the lane's rows
+    u32x2_t k, q;         // the lane's 4 rows of k and q (bf16)
+    u32x4_t v;            // the lane's 8 columns of v (bf16)
+    u32x4_t gk;           // the lane's 4 rows of gk (f32)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *p, int bytes)
@@ -228,16 +240,58 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *p, int bytes
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
 
+// Sum over the four 16-lane rows of a wave, in every lane.
+__device__ __forceinline__ float rows_sum(float x)
+{
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Transposing reduction over the four 16-lane rows: given per-lane partials
+// x0..x3, returns in lane row r the total over the rows of x_r.
+__device__ __forceinline__ float rows_reduce4(float x0, float x1, float x2, float x3)
+{
+    // rows (0, 1, 2, 3) of a: x0 over rows {0,2}, {1,3}; x2 likewise
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x2), false, false);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x1), __float_as_uint(x3), false, false);
+    const float A = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float C = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+    const auto d = __builtin_amdgcn_permlane16_swap(__float_as_uint(A), __float_as_uint(C), false, false);
+    return __uint_as_float(d[0]) + __uint_as_float(d[1]);
+}
+
+// Broadcast of each 16-lane row's value: y[r] holds row r's x in every row.
+__device__ __forceinline__ void rows_gather(float x, float y[4])
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const auto e = __builtin_amdgcn_permlane32_swap(a[0], a[0], false, false);
+    const auto o = __builtin_amdgcn_permlane32_swap(a[1], a[1], false, false);
+    y[0] = __uint_as_float(e[0]);
+    y[2] = __uint_as_float(e[1]);
+    y[1] = __uint_as_float(o[0]);
+    y[3] = __uint_as_float(o[1]);
+}
+
+__device__ __forceinline__ void s1_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <bool GK>
-__global__ __launch_bounds__(256) void decode_s1_kernel(DecodeParams p, int ntiles)
+__global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, int nheads)
 {
     using namespace s1;
+    __shared__ float4 red[2][NW][64];
+    __shared__ float redkq[2][NW];
+
     const int lane = threadIdx.x & 63;
-    const int w = uniform(blockIdx.x * WPB + (threadIdx.x >> 6));
-    const int G = uniform(gridDim.x * WPB);
+    const int j = uniform(threadIdx.x >> 6);
+    const int G = gridDim.x;
     const int Nv = p.Nv, rep = p.Nv / p.Nk;
-    const int rg = lane % RG, cg = lane / RG;
-    const int row0 = rg * RPL;
+    const int lr = lane >> 4, cg = lane & 15;
+    const int row0 = j * RW + lr * NI;   // the lane's first row
 
     const bf16_t *q = static_cast<const bf16_t *>(p.q);
     const bf16_t *k = static_cast<const bf16_t *>(p.k);
@@ -250,18 +304,10 @@ __global__ __launch_bounds__(256) void decode_s1_kernel(DecodeParams p, int ntil
     const int32_t *g_src = p.g ? reinterpret_cast<const int32_t *>(p.g) : p.lens;
     const int32_t *beta_src = static_cast<const int32_t *>(p.beta);
 
-    auto coords = [&](int tile, int &b, int &h, int &ct) __attribute__((always_inline)) {
-        const int tt = tile < ntiles ? tile : 0;
-        ct = tt % NT;
-        const int bh = tt / NT;
-        h = bh % Nv;
-        b = bh / Nv;
-    };
-    // Issues the scalar loads of a tile (they complete while the wave works).
-    auto scal = [&](int tile) __attribute__((always_inline)) {
-        int b, h, ct;
-        coords(tile, b, h, ct);
-        const size_t vh = (size_t)b * Nv + h;
+    auto scal = [&](int hd) __attribute__((always_inline)) {
+        const int hc = hd < nheads ? hd : nheads - 1;
+        const int b = hc / Nv, h = hc % Nv;
+        const int vh = b * Nv + h;
         S1Scal c;
         c.len = ld_const(p.lens, b);
         c.nacc = ld_const(nacc_src, b);
@@ -270,145 +316,185 @@ __global__ __launch_bounds__(256) void decode_s1_kernel(DecodeParams p, int ntil
         c.g = ld_const(g_src, p.g ? vh : 0);
         return c;
     };
-    // Resolves a tile from its scalars and issues its vector loads.
-    auto vec = [&](S1Regs &R, S1Tile &t, const S1Scal &c, int tile) __attribute__((always_inline)) {
-        coords(tile, t.b, t.h, t.ct);
-        const size_t vh = (size_t)t.b * Nv + t.h;
+    // Resolves a head from its scalars and issues all of its loads.
+    auto load = [&](S1Head &H, const S1Scal &c, int hd) __attribute__((always_inline)) {
+        const int hc = hd < nheads ? hd : nheads - 1;
+        H.b = hc / Nv;
+        H.h = hc % Nv;
+        const int vh = H.b * Nv + H.h;
         const int L = c.len < 0 ? 0 : (c.len > 1 ? 1 : c.len);
         const int n = p.nacc ? c.nacc : L;
-        const int r = (tile < ntiles && L == 1 && n == 1) ? c.idx : -1;
-        t.r = (r >= 0 && r < p.slots) ? r : -1;
-        t.beta = __uint_as_float(((uint32_t)c.beta2 >> (16 * (int)(vh & 1))) << 16);
-        t.g = p.g ? __int_as_float(c.g) : 0.f;
-        const bool on = t.r >= 0;
-        const size_t qk = (size_t)t.b * p.Nk + t.h / rep;
-        const int col = t.ct * TV;
-        const auto srs = brsrc(pool + ((size_t)(on ? t.r : 0) * Nv + t.h) * DK * DV + col, on ? (DK * DV - col) * 2 : 0);
+        const int r = (hd < nheads && L == 1 && n == 1) ? c.idx : -1;
+        H.r = (r >= 0 && r < p.slots) ? r : -1;
+        H.beta = __uint_as_float(((uint32_t)c.beta2 >> (16 * (vh & 1))) << 16);
+        H.g = p.g ? __int_as_float(c.g) : 0.f;
+        const bool on = H.r >= 0;
+        const auto srs = brsrc(pool + ((size_t)(on ? H.r : 0) * Nv + H.h) * DK * DV, on ? DK * DV * 2 : 0);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i)
-            R.st[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * VEC) * 2, 0, 0);
+        for (int i = 0; i < NI; ++i)
+            H.st[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+        const size_t qk = (size_t)H.b * p.Nk + H.h / rep;
         const int tb = on ? DK * 2 : 0;
-        R.k = __builtin_amdgcn_raw_buffer_load_b128(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
-        R.q = __builtin_amdgcn_raw_buffer_load_b128(brsrc(q + qk * DK, tb), row0 * 2, 0, 0);
-        R.v = __builtin_amdgcn_raw_buffer_load_b128(brsrc(v + vh * DV + col, on ? (DV - col) * 2 : 0), cg * VEC * 2, 0, 0);
-        if constexpr (GK) {
-            const auto grs = brsrc(p.gk + vh * DK, on ? DK * 4 : 0);
-            R.gk[0] = __builtin_amdgcn_raw_buffer_load_b128(grs, row0 * 4, 0, 0);
-            R.gk[1] = __builtin_amdgcn_raw_buffer_load_b128(grs, row0 * 4 + 16, 0, 0);
-        }
+        H.k = __builtin_amdgcn_raw_buffer_load_b64(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
+        H.q = __builtin_amdgcn_raw_buffer_load_b64(brsrc(q + qk * DK, tb), row0 * 2, 0, 0);
+        H.v = __builtin_amdgcn_raw_buffer_load_b128(brsrc(v + (size_t)vh * DV, on ? DV * 2 : 0), cg * 16, 0, 0);
+        if constexpr (GK)
+            H.gk = __builtin_amdgcn_raw_buffer_load_b128(brsrc(p.gk + (size_t)vh * DK, on ? DK * 4 : 0), row0 * 4, 0, 0);
     };
-    // A tile that is skipped still waits for its (empty) loads, so that every
-    // path leaves the register set settled: otherwise the compiler has to wait
-    // for it where the paths meet, before the next prefetch is issued.
-    auto settle = [&](const S1Regs &R) __attribute__((always_inline)) {
-        uint32_t x = R.k.x ^ R.q.x ^ R.v.x;
+    // A skipped head still waits for its (empty) loads, so that every path
+    // leaves the register sets settled: otherwise the compiler has to wait
+    // for them where the paths meet, before the next prefetch is issued.
+    auto settle = [&](const S1Head &H) __attribute__((always_inline)) {
+        uint32_t x = H.k.x ^ H.q.x ^ H.v.x;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) x ^= R.st[i].x ^ R.st[i].w;
-        if constexpr (GK) x ^= R.gk[0].x ^ R.gk[1].x;
+        for (int i = 0; i < NI; ++i) x ^= H.st[i].x ^ H.st[i].w;
+        if constexpr (GK) x ^= H.gk.x;
         asm volatile("" ::"v"(x));
     };
-    auto compute = [&](const S1Regs &R, const S1Tile &t, int tile) __attribute__((always_inline)) {
-        if (tile >= ntiles) {
-            settle(R);
+    // Output columns of this lane in the writing wave: 8 cg + 2 lr, + 1.
+    auto out_ptr = [&](const S1Head &H) __attribute__((always_inline)) {
+        return reinterpret_cast<uint32_t *>(out + ((size_t)H.b * Nv + H.h) * DV + cg * 8 + lr * 2);
+    };
+    int par = 0;
+    auto compute = [&](const S1Head &H) __attribute__((always_inline)) {
+        if (H.r < 0) {
+            settle(H);
+            if (j == 0) *out_ptr(H) = 0u;
             return;
         }
-        const size_t vh = (size_t)t.b * Nv + t.h;
-        const int col = t.ct * TV + cg * VEC;
-        bf16_t *op = out + vh * DV + col;
-        if (t.r < 0) {
-            settle(R);
-            if (rg == 0) *reinterpret_cast<u32x4_t *>(op) = u32x4_t{0u, 0u, 0u, 0u};
-            return;
-        }
-        // D = exp(g) exp(gk_i)
-        const float a = __expf(t.g);
-        const uint32_t kw[4] = {R.k.x, R.k.y, R.k.z, R.k.w}, qw[4] = {R.q.x, R.q.y, R.q.z, R.q.w};
-        float dd[RPL];
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) dd[i] = a;
+        const float a = __expf(H.g);
+        float dd[NI];
         if constexpr (GK) {
-            const uint32_t gw[8] = {R.gk[0].x, R.gk[0].y, R.gk[0].z, R.gk[0].w, R.gk[1].x, R.gk[1].y, R.gk[1].z, R.gk[1].w};
+            dd[0] = a * __expf(__uint_as_float(H.gk.x));
+            dd[1] = a * __expf(__uint_as_float(H.gk.y));
+            dd[2] = a * __expf(__uint_as_float(H.gk.z));
+            dd[3] = a * __expf(__uint_as_float(H.gk.w));
+        } else {
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) dd[i] = a * __expf(__uint_as_float(gw[i]));
+            for (int i = 0; i < NI; ++i) dd[i] = a;
         }
-        float kr[RPL], dk[RPL], dq[RPL], kq = 0.f;
+        const float kr[NI] = {bf16_lo(H.k.x), bf16_hi(H.k.x), bf16_lo(H.k.y), bf16_hi(H.k.y)};
+        // Partial S^T (D k) and S^T (D q) over the lane's rows.
+        uint32_t sw[NI][4];
+        float kv[8], sq[8], kq = 0.f;
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const float ki = (i & 1) ? bf16_hi(kw[i >> 1]) : bf16_lo(kw[i >> 1]);
-            const float qi = (i & 1) ? bf16_hi(qw[i >> 1]) : bf16_lo(qw[i >> 1]);
-            kr[i] = ki;
-            dk[i] = dd[i] * ki;
-            dq[i] = dd[i] * qi;
-            kq = fmaf(ki, qi, kq);
-        }
-        // One pass over S: S^T (D k) and S^T (D q) for this lane's columns.
-        float st[RPL][VEC];
-        float kv[VEC], sq[VEC];
+        for (int c = 0; c < 8; ++c) { kv[c] = 0.f; sq[c] = 0.f; }
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) { kv[c] = 0.f; sq[c] = 0.f; }
+        for (int i = 0; i < NI; ++i) { sw[i][0] = H.st[i].x; sw[i][1] = H.st[i].y; sw[i][2] = H.st[i].z; sw[i][3] = H.st[i].w; }
+        if constexpr (GK) {
+            const float qr[NI] = {bf16_lo(H.q.x), bf16_hi(H.q.x), bf16_lo(H.q.y), bf16_hi(H.q.y)};
+            float dk[NI], dq[NI];
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const uint32_t sw[4] = {R.st[i].x, R.st[i].y, R.st[i].z, R.st[i].w};
+            for (int i = 0; i < NI; ++i) {
+                dk[i] = dd[i] * kr[i];
+                dq[i] = dd[i] * qr[i];
+                kq = fmaf(kr[i], qr[i], kq);
+            }
 #pragma unroll
-            for (int c = 0; c < VEC; ++c) {
-                st[i][c] = (c & 1) ? bf16_hi(sw[c >> 1]) : bf16_lo(sw[c >> 1]);
-                kv[c] = fmaf(st[i][c], dk[i], kv[c]);
-                sq[c] = fmaf(st[i][c], dq[i], sq[c]);
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const float s = (c & 1) ? bf16_hi(sw[i][c >> 1]) : bf16_lo(sw[i][c >> 1]);
+                    kv[c] = fmaf(s, dk[i], kv[c]);
+                    sq[c] = fmaf(s, dq[i], sq[c]);
+                }
+        } else {
+            // One decay for all rows: the sums run over bf16 pairs of rows
+            // (v_dot2_f32_bf16, exact products) and take exp(g) afterwards.
+            const uint32_t kp[2] = {H.k.x, H.k.y}, qp[2] = {H.q.x, H.q.y};
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const bf16x2_t kb = __builtin_bit_cast(bf16x2_t, kp[pr]), qb = __builtin_bit_cast(bf16x2_t, qp[pr]);
+                kq = __builtin_amdgcn_fdot2_f32_bf16(kb, qb, kq, false);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    // (S[2pr][2u], S[2pr+1][2u]) and (S[2pr][2u+1], S[2pr+1][2u+1])
+                    const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(sw[2 * pr + 1][u], sw[2 * pr][u], 0x05040100u));
+                    const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(sw[2 * pr + 1][u], sw[2 * pr][u], 0x07060302u));
+                    kv[2 * u] = __builtin_amdgcn_fdot2_f32_bf16(lo, kb, kv[2 * u], false);
+                    sq[2 * u] = __builtin_amdgcn_fdot2_f32_bf16(lo, qb, sq[2 * u], false);
+                    kv[2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, kb, kv[2 * u + 1], false);
+                    sq[2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, qb, sq[2 * u + 1], false);
+                }
             }
         }
+        // Over the wave: lane row r keeps the totals of columns 8 cg + 2r, + 1.
+        float4 t;
+        t.x = rows_reduce4(kv[0], kv[2], kv[4], kv[6]);
+        t.y = rows_reduce4(kv[1], kv[3], kv[5], kv[7]);
+        t.z = rows_reduce4(sq[0], sq[2], sq[4], sq[6]);
+        t.w = rows_reduce4(sq[1], sq[3], sq[5], sq[7]);
+        kq = rows_sum(kq);
+        // Over the workgroup.
+        red[par][j][lane] = t;
+        if (lane == 0) redkq[par][j] = kq;
+        s1_barrier();
+        float4 u = red[par][0][lane];
 #pragma unroll
-        for (int c = 0; c < VEC; ++c) { kv[c] = group_sum<RG>(kv[c]); sq[c] = group_sum<RG>(sq[c]); }
-        kq = group_sum<RG>(kq);
-        // delta, the updated state (stored at once), then the output.
-        const uint32_t vw[4] = {R.v.x, R.v.y, R.v.z, R.v.w};
-        float dl[VEC];
-#pragma unroll
-        for (int c = 0; c < VEC; ++c) dl[c] = t.beta * (((c & 1) ? bf16_hi(vw[c >> 1]) : bf16_lo(vw[c >> 1])) - kv[c]);
-        const auto srs = brsrc(pool + ((size_t)t.r * Nv + t.h) * DK * DV + t.ct * TV, (DK * DV - t.ct * TV) * 2);
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            uint32_t ow[4];
-#pragma unroll
-            for (int c = 0; c < VEC; c += 2)
-                ow[c >> 1] = pack_bf16x2(fmaf(st[i][c], dd[i], kr[i] * dl[c]), fmaf(st[i][c + 1], dd[i], kr[i] * dl[c + 1]));
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, srs, ((row0 + i) * DV + cg * VEC) * 2, 0, 0);
+        for (int w = 1; w < NW; ++w) {
+            const float4 x = red[par][w][lane];
+            u.x += x.x; u.y += x.y; u.z += x.z; u.w += x.w;
         }
-        if (rg == 0) {
+        kq = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) kq += redkq[par][w];
+        par ^= 1;
+        if constexpr (!GK) { u.x *= a; u.y *= a; u.z *= a; u.w *= a; }
+        // delta of this lane row's two columns, then of all eight.
+        const uint32_t vw = lr == 0 ? H.v.x : lr == 1 ? H.v.y : lr == 2 ? H.v.z : H.v.w;
+        const float d0 = H.beta * (bf16_lo(vw) - u.x), d1 = H.beta * (bf16_hi(vw) - u.y);
+        if (j == 0)
+            *out_ptr(H) = pack_bf16x2(p.scale * fmaf(d0, kq, u.z), p.scale * fmaf(d1, kq, u.w));
+        float e0[4], e1[4], dl[8];
+        rows_gather(d0, e0);
+        rows_gather(d1, e1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { dl[2 * r] = e0[r]; dl[2 * r + 1] = e1[r]; }
+        // S' = D S + k delta^T, stored at once.
+        const auto srs = brsrc(pool + ((size_t)H.r * Nv + H.h) * DK * DV, DK * DV * 2);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            // The packed words are widened afresh rather than kept widened
+            // across the reductions.
+            asm volatile("" : "+v"(sw[i][0]), "+v"(sw[i][1]), "+v"(sw[i][2]), "+v"(sw[i][3]));
             uint32_t ow[4];
 #pragma unroll
-            for (int c = 0; c < VEC; c += 2)
-                ow[c >> 1] = pack_bf16x2(p.scale * fmaf(dl[c], kq, sq[c]), p.scale * fmaf(dl[c + 1], kq, sq[c + 1]));
-            *reinterpret_cast<u32x4_t *>(op) = u32x4_t{ow[0], ow[1], ow[2], ow[3]};
+            for (int c = 0; c < 8; c += 2)
+                ow[c >> 1] = pack_bf16x2(fmaf(bf16_lo(sw[i][c >> 1]), dd[i], kr[i] * dl[c]),
+                                         fmaf(bf16_hi(sw[i][c >> 1]), dd[i], kr[i] * dl[c + 1]));
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, srs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
         }
     };
 
-    // Half-step for tile i (register set X): consume the scalars of tile
-    // i + G (issued one half-step earlier) and issue its vector loads into the
-    // other set; then issue the scalars of tile i + 2G; then compute tile i.
-    // The scheduling barriers keep each wait for scalars clear of the loads
-    // issued after it.
-    S1Regs A, B;
-    S1Tile tA, tB;
-    S1Scal cX, cY;
-    int tile = w;
-    cX = scal(tile);
-    vec(A, tA, cX, tile);
-    cY = scal(tile + G);
+    // The loads of the heads up to hd + (NB - 1) G are in flight while head
+    // hd is computed, and the scalars of the head after them; the NB register
+    // sets rotate. The scheduling barriers keep each wait for scalars clear
+    // of the scalar loads issued after it.
+    S1Head H[NB];
+    S1Scal C[NB];
+    int hd = blockIdx.x;
+#pragma unroll
+    for (int m = 0; m + 1 < NB; ++m) {
+        C[m] = scal(hd + m * G);
+        load(H[m], C[m], hd + m * G);
+    }
+    C[NB - 1] = scal(hd + (NB - 1) * G);
+    auto step = [&](auto mc) __attribute__((always_inline)) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int f = (m + NB - 1) % NB;
+        load(H[f], C[f], hd + (NB - 1) * G);
+        __builtin_amdgcn_sched_barrier(0);
+        C[m] = scal(hd + NB * G);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(H[m]);
+        hd += G;
+        return hd >= nheads;
+    };
     while (true) {
-        vec(B, tB, cY, tile + G);
-        __builtin_amdgcn_sched_barrier(0);
-        cX = scal(tile + 2 * G);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(A, tA, tile);
-        tile += G;
-        if (tile >= ntiles) break;
-        vec(A, tA, cX, tile + G);
-        __builtin_amdgcn_sched_barrier(0);
-        cY = scal(tile + 2 * G);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(B, tB, tile);
-        tile += G;
-        if (tile >= ntiles) break;
+        if (step(std::integral_constant<int, 0>{})) break;
+        if (step(std::integral_constant<int, 1>{})) break;
+        if constexpr (NB > 2) { if (step(std::integral_constant<int, 2 % NB>{})) break; }
+        if constexpr (NB > 3) { if (step(std::integral_constant<int, 3 % NB>{})) break; }
     }
 }
 
@@ -454,12 +540,11 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
 {
     if (dtype == 1 && p.S == 1 && Dk == s1::DK && Dv == s1::DV) {
         *supported = true;
-        const int ntiles = p.B * p.Nv * s1::NT;
-        const int waves = ntiles < s1::WAVES ? ntiles : s1::WAVES;
-        const dim3 grid((unsigned)((waves + s1::WPB - 1) / s1::WPB)), block(64 * s1::WPB);
+        const int nheads = p.B * p.Nv;
+        const dim3 grid((unsigned)(nheads < s1::GROUPS ? nheads : s1::GROUPS)), block(64 * s1::NW);
         DecodeParams pc = p;
-        int nt = ntiles;
-        void *args[] = {&pc, &nt};
+        int nh = nheads;
+        void *args[] = {&pc, &nh};
         const void *fn = p.gk ? (const void *)decode_s1_kernel<true> : (const void *)decode_s1_kernel<false>;
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
