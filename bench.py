@@ -202,6 +202,7 @@ def chunk_calls(c, copies):
         a = gdr.ChunkArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S, c.Dk,
                           c.Dv, c.chunk, p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["g"]),
                           p(t["init"]), p(t["lens"]), c.scale, p(t["out"]), p(t["fin"]))
+        t["ws"] = gdr.chunk_workspace(a, torch.device("cuda"))
         keep.append((t, a))
 
         def call(a=a):

@@ -48,6 +48,7 @@ class ChunkArgs(ctypes.Structure):
         ("q", _vp), ("k", _vp), ("v", _vp), ("beta", _vp), ("g", _vp),
         ("initial_state", _vp), ("actual_seq_lengths", _vp),
         ("scale_value", ctypes.c_float), ("out", _vp), ("final_state", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdr_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
     lib.gdr_chunk.restype = ctypes.c_int
     lib.gdr_chunk.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
+    lib.gdr_chunk_workspace_size.restype = ctypes.c_int64
+    lib.gdr_chunk_workspace_size.argtypes = [ctypes.POINTER(ChunkArgs)]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_abi_version.restype = ctypes.c_int32
@@ -186,5 +189,21 @@ def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None
     a = ChunkArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, int(chunk_size),
                   _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
                   _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state))
-    _check(load_library().gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")
+    lib = load_library()
+    ws = chunk_workspace(a, dev)
+    _check(lib.gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")
+    del ws   # stream-ordered reuse by the caching allocator is safe after the enqueue
     return out, final_state
+
+
+def chunk_workspace(a, dev):
+    """Allocates the workspace gdr_chunk needs for the arguments `a` (a
+    ChunkArgs) on `dev`, stores it in `a` and returns the tensor, which must
+    stay alive until the call has been enqueued."""
+    n = int(load_library().gdr_chunk_workspace_size(ctypes.byref(a)))
+    if n <= 0:
+        a.workspace, a.workspace_bytes = None, 0
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), n
+    return ws

@@ -63,6 +63,13 @@ gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
     return from_launch(e, ok);
 }
 
+int64_t gdr_chunk_workspace_size(const gdr_chunk_args *a)
+{
+    if (!a) return -1;
+    if (a->B < 0 || a->S < 0 || a->Nv < 1) return 0;
+    return gdr::chunk_workspace_bytes(a->dtype, a->Dk, a->Dv, a->chunk_size, a->B, a->Nv, a->S);
+}
+
 gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
 {
     if (!a) return GDR_ERR_NULL;
@@ -73,8 +80,15 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     if (a->B == 0) return GDR_OK;
     if (!a->q || !a->k || !a->v || !a->beta || !a->out || !a->final_state) return GDR_ERR_NULL;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) ||
-        !aligned16(a->initial_state) || !aligned16(a->final_state))
+        !aligned16(a->initial_state) || !aligned16(a->final_state) || !aligned16(a->workspace))
         return GDR_ERR_UNSUPPORTED;
+    // 32-bit offsets inside the kernels: one head plane and the chunk count.
+    if ((int64_t)a->S * a->Dk * 4 > 0x7fffffffLL || (int64_t)a->S * a->Dv * 4 > 0x7fffffffLL ||
+        (int64_t)a->B * a->Nv * (a->S / a->chunk_size + 1) > 0x7ffffff0LL)
+        return GDR_ERR_UNSUPPORTED;
+    const int64_t need = gdr_chunk_workspace_size(a);
+    if (need > 0 && !a->workspace) return GDR_ERR_NULL;
+    if (need > a->workspace_bytes) return GDR_ERR_SHAPE;
 
     gdr::ChunkParams p;
     p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta;
@@ -83,6 +97,7 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     p.lens = a->actual_seq_lengths;
     p.out = a->out;
     p.fin = a->final_state;
+    p.work = a->workspace;
     p.scale = a->scale_value;
     p.B = a->B; p.Nk = a->Nk; p.Nv = a->Nv; p.S = a->S;
     bool ok = false;

@@ -19,18 +19,14 @@
 // chunk enter as identity steps (k = q = v = beta = 0, g = 0) by selection,
 // so padded inputs are never read; their outputs are written as exact zeros.
 //
-// Two kernels:
-//  * chunk_mfma_kernel — bf16 I/O, Dk = Dv = 128, C = 64. One workgroup of
-//    eight wavefronts per (sequence, value head, 64-column tile of Dv); the
-//    columns of S evolve independently, so each tile carries its own slice of
-//    the state through all chunks in float32 MFMA accumulators. All dense
-//    products run on v_mfma_f32_16x16x32_bf16 with bf16 operands staged in LDS
-//    in the layout each operand needs (16-byte reads). T is never formed:
-//    each 16x16 diagonal block of (I + A) is inverted as the finite product
-//    (I - A)(I + A^2)(I + A^4)(I + A^8) (A is nilpotent of index 16) in
-//    registers with v_mfma_f32_16x16x16_bf16 (a result's register layout is
-//    directly the right-hand operand layout, and its transpose the left-hand
-//    one), and (I + A) Vnew = X is solved by block forward substitution.
+// Kernels:
+//  * chunk_t_kernel + chunk_mfma_kernel — bf16 I/O, Dk = Dv = 128, C = 64.
+//    chunk_t_kernel forms T = (I + A)^-1 of every chunk of every sequence in
+//    parallel (it depends on k, beta and g only) into the caller's workspace;
+//    chunk_mfma_kernel then makes one pass over the chunks per (sequence,
+//    value head, 64-column tile of Dv), carrying its slice of the state in
+//    float32 matrix-core accumulators. All dense products run on
+//    v_mfma_f32_32x32x16_bf16 with bf16 operands.
 //  * chunk_f32_kernel — float32 I/O, small heads. The same chunk algorithm in
 //    plain float32 arithmetic; T by row-wise forward substitution.
 #include <atomic>
@@ -42,29 +38,8 @@ namespace gdr {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4_t mma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4_t mma16(bf16x4_t a, bf16x4_t b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ bf16x4_t to_bf4(f32x4_t x)
-{
-    bf16x4_t r;
-    r[0] = (__bf16)x[0]; r[1] = (__bf16)x[1]; r[2] = (__bf16)x[2]; r[3] = (__bf16)x[3];
-    return r;
-}
-__device__ __forceinline__ f32x4_t zero4()
-{
-    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    return z;
-}
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
@@ -146,9 +121,7 @@ constexpr int SET_BYTES = 66560;
 constexpr int P_VT = 2 * SET_BYTES;  // V^T rows (value columns), tokens in k-order [64][128 B]
 constexpr int P_TP = P_VT + 8192;    // T diag(beta exp(gamma)) rows, k-order     [64][128 B]
 constexpr int P_TB = P_TP + 8192;    // T diag(beta) rows, k-order                [64][128 B]
-constexpr int P_A10 = P_TB + 8192;   // operand of A_10^T, register order         [2][64][16 B]
-constexpr int P_Z = P_A10 + 2048;    // operand of -(T_11 A_10)^T, register order [2][64][16 B]
-constexpr int P_BG = P_Z + 2048;     // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
+constexpr int P_BG = P_TB + 8192;    // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
 constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
 constexpr int LDS_BYTES = P_FLAG + 64;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -179,6 +152,11 @@ __device__ __forceinline__ float wave_prefix_sum(float x)
     return x;
 }
 
+// 16 consecutive elements (pieces a, b) into k-order: slots 0-3 and 12-15
+// stay, slots 4-7 take elements 8-11, slots 8-11 elements 4-7.
+__device__ __forceinline__ u32x4_t korder_lo(u32x4_t a, u32x4_t b) { return u32x4_t{a.x, a.y, b.x, b.y}; }
+__device__ __forceinline__ u32x4_t korder_hi(u32x4_t a, u32x4_t b) { return u32x4_t{a.z, a.w, b.z, b.w}; }
+
 // Arrival counters (LDS) that order the prep waves among themselves without
 // holding up the chain waves. Counters only grow; a wave waits for the count
 // that the current chunk's arrivals reach. LDS operations of one wave complete
@@ -194,6 +172,172 @@ __device__ __forceinline__ void wait_for(uint32_t *f, uint32_t target)
     asm volatile("" ::: "memory");
 }
 
+// T = (I + A)^-1 of every chunk, ahead of the pass over the chunks: T depends
+// on k, beta and g of its chunk only, never on the state, so all chunks of
+// all sequences are independent. One wavefront per (sequence, value head,
+// chunk), with no exchange between wavefronts: the K operands come from
+// memory straight into registers, already in k-order, and every product
+// stays in the wave.
+//   Gram blocks G_00, G_11 (K_d K_d^T) and G_10 (K_1 K_0^T);
+//   -A_dd = -(diag(beta) G_dd) * exp(gamma_r - gamma_i) (strictly lower) and
+//   T_dd as the finite product (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16)
+//   (A_dd is nilpotent of index 32), powers by squaring;
+//   T_10 = -T_11 A_10 T_00.
+// T is stored in result-register order, so that every store is 1 KB
+// contiguous: per chunk, block j (0: T_00, 1: T_11, 2: T_10) and k-step s hold
+// op8 of the block's 32x32 result, 16 bytes per lane: row r = c32 of the block
+// holds columns (k-order piece 2s + hh) at ((2j + s) * 64 + lane) * 16 bytes.
+// The block T_01 = 0 is neither written nor read; 6 KB of the 8 KB per chunk
+// are used.
+namespace tk {
+constexpr int WAVES = 4;                  // independent wavefronts per workgroup
+constexpr int CHUNK_ELEMS = 64 * 64;      // workspace elements per chunk
+// Byte offset in a chunk's T of piece `piece` (k-order, 0-7) of row r (0-63).
+__device__ __forceinline__ int piece_offset(int r, int piece)
+{
+    const int j = r < 32 ? 0 : (piece >= 4 ? 1 : 2);
+    const int s = (piece & 3) >> 1, hh = piece & 1;
+    return ((2 * j + s) * 64 + (r & 31) + 32 * hh) * 16;
+}
+}  // namespace tk
+
+// D((I + A_dd)^-1 ^T) for one 32x32 diagonal block, from its Gram block G
+// (D layout) and beta, gamma log2(e) of its rows (br, gr: the 16 rows this
+// lane holds) and of its column c32 (bc, gc).
+__device__ __forceinline__ f32x16_t diag_inverse_t(const f32x16_t &G, const float *br, const float *gr, float bc,
+                                                   float gc, int c32, int hh)
+{
+    // N = D(-A_dd), Nt = D(-A_dd^T), R = D((I - A_dd)^T). At each position
+    // only one of A_dd, A_dd^T can be nonzero (G is symmetric), so one
+    // exponential serves both.
+    f32x16_t N, Nt, R;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int rl = drow(q, hh);
+        const bool below = c32 < rl;
+        const float dg = gr[q] - gc;
+        const float a = -__builtin_amdgcn_exp2f(below ? dg : -dg) * (below ? br[q] : bc) * G[q];
+        N[q] = below ? a : 0.f;
+        Nt[q] = rl < c32 ? a : 0.f;
+        R[q] = rl == c32 ? 1.f : Nt[q];
+    }
+    // R_{k+1}^T = R_k^T + (N^(2^k))^T R_k^T, powers by squaring.
+    f32x16_t M = prod(Nt, N, zero16()), Mt = prod(N, Nt, zero16());   // N^2
+    R = prod(M, R, R);
+    f32x16_t M2 = prod(Mt, M, zero16()), M2t = prod(M, Mt, zero16());  // N^4
+    R = prod(M2, R, R);
+    M = prod(M2t, M2, zero16());
+    Mt = prod(M2, M2t, zero16());                                     // N^8
+    R = prod(M, R, R);
+    M2 = prod(Mt, M, zero16());                                       // N^16
+    return prod(M2, R, R);
+}
+
+__global__ __launch_bounds__(64 * tk::WAVES) void chunk_t_kernel(ChunkParams p, int nchk, int units)
+{
+    using namespace mk;
+    // A few floats per wave: beta and gamma log2(e) of the chunk's tokens.
+    __shared__ __align__(16) float bgs[tk::WAVES][128];
+    const int Nk = p.Nk, Nv = p.Nv, S = p.S;
+    const int rep = Nv / Nk;
+    const int lane = threadIdx.x & 63, wl = uniform(threadIdx.x >> 6);
+    const int hh = lane >> 5, c32 = lane & 31;
+    // Unit order: value heads of one key head, then chunks, then (b, key
+    // head): the waves of a workgroup share k through the cache.
+    const int u = blockIdx.x * tk::WAVES + wl;
+    if (u >= units) return;
+    const int hr = u % rep;
+    const int c = (u / rep) % nchk;
+    const int bk = u / (rep * nchk);
+    const int kh = bk % Nk, b = bk / Nk;
+    const int h = kh * rep + hr;
+    int L = p.lens ? ld_const(p.lens, b) : S;
+    L = L < 0 ? 0 : (L > S ? S : L);
+    const int t0 = c * C;
+    if (t0 >= L) return;
+
+    // K operands: row 32d + c32 of the chunk; k-step ks takes features
+    // 16ks + 8hh .. + 7. The Gram blocks contract over the features, so any
+    // order serves as long as both operands share it. Rows past L read as zeros.
+    const bf16_t *kb = static_cast<const bf16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, L * DK * 2, 0x00020000);
+    bf16x8_t kf[2][8];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            kf[d][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         krs, ((t0 + 32 * d + c32) * DK + 16 * ks + 8 * hh) * 2, 0, 0));
+    // beta and the in-chunk cumulative log decay (lane t = token t0 + t).
+    {
+        const size_t vh = (size_t)b * Nv + h;
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const bf16_t *>(p.beta) + vh * S), (short)0, L * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.g ? p.g + vh * S : nullptr), (short)0, p.g ? L * 4 : 0, 0x00020000);
+        const uint32_t rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
+        const uint32_t rg = __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
+        bgs[wl][lane] = __uint_as_float(rb << 16);
+        bgs[wl][64 + lane] = wave_prefix_sum(__uint_as_float(rg)) * 1.44269504088896340736f;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's own writes, read below
+    }
+    const float *bg = bgs[wl], *gv = bgs[wl] + 64;
+    // beta / gamma of the rows a lane holds in a result tile: rows 8m + 4hh + i
+    // of the 32-row block starting at r0.
+    auto rows4 = [&](const float *v, int r0, float *o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 x = *reinterpret_cast<const float4 *>(v + r0 + 8 * m + 4 * hh);
+            o[4 * m] = x.x; o[4 * m + 1] = x.y; o[4 * m + 2] = x.z; o[4 * m + 3] = x.w;
+        }
+    };
+
+    f32x16_t G0 = zero16(), G1 = zero16(), G10 = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        G0 = mfma32(kf[0][ks], kf[0][ks], G0);
+        G1 = mfma32(kf[1][ks], kf[1][ks], G1);
+        G10 = mfma32(kf[1][ks], kf[0][ks], G10);
+    }
+    // A_10 (rows 32-63 of A against columns 0-31; no mask needed).
+    float br1[16], gr1[16];
+    rows4(bg, 32, br1);
+    rows4(gv, 32, gr1);
+    {
+        const float gi = gv[c32];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) G10[q] *= br1[q] * __builtin_amdgcn_exp2f(gr1[q] - gi);
+    }
+    unsigned char *tw = static_cast<unsigned char *>(p.work) + (((size_t)b * Nv + h) * nchk + c) * tk::CHUNK_ELEMS * 2;
+    // k-step s of block j, in register order.
+    auto put = [&](int j, int s, bf16x8_t v) __attribute__((always_inline)) {
+        *reinterpret_cast<bf16x8_t *>(tw + ((2 * j + s) * 64 + lane) * 16) = v;
+    };
+    // T_11, then Z = -(T_11 A_10)^T = -A_10^T T_11^T.
+    const f32x16_t R1 = diag_inverse_t(G1, br1, gr1, bg[32 + c32], gv[32 + c32], c32, hh);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) put(1, s, op8(R1, s));
+    f32x16_t Z = -prod(G10, R1, zero16());
+    // T_00, then T_10^T = T_00^T Z with D(T_00) from D(T_00^T) and the identity.
+    float br0[16], gr0[16];
+    rows4(bg, 0, br0);
+    rows4(gv, 0, gr0);
+    const f32x16_t R0 = diag_inverse_t(G0, br0, gr0, bg[c32], gv[c32], c32, hh);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) put(0, s, op8(R0, s));
+    bf16x8_t eye[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
+    f32x16_t T0 = mfma32(op8(R0, 0), eye[0], zero16());
+    T0 = mfma32(op8(R0, 1), eye[1], T0);
+    const f32x16_t T10 = prod(T0, Z, zero16());
+#pragma unroll
+    for (int s = 0; s < 2; ++s) put(2, s, op8(T10, s));
+}
+
 // One workgroup per (sequence, value head, 64-column tile of Dv); the columns
 // of S evolve independently, so each tile carries its own slice of the state.
 // The chunk step is split so that only two products depend on the state:
@@ -207,13 +351,11 @@ __device__ __forceinline__ void wait_for(uint32_t *f, uint32_t target)
 // and run these three products for chunk c; their operands never leave
 // registers except W, Q, P, K^T and U, read from the chunk's operand set.
 // Prep waves (0-5) build the operand set of chunk c + 1 meanwhile:
-//   stage K, Q, V (loaded from HBM one chunk earlier) in k-order;
-//   Gram blocks: wave 0/1 the diagonal blocks of K K^T, wave 2 the block
-//     below them, waves 3-5 the three nonzero blocks of P;
-//   waves 0/1 invert (I + A_dd) as the finite product
-//     (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16) (A_dd is nilpotent of
-//     index 32), then T_10 = -T_11 A_10 T_00 (waves 1 and 0);
-//   waves 2-5 transpose K and V (a product with the identity, exact);
+//   stage K, Q, V and this chunk's T (loaded one chunk earlier) in k-order;
+//   every lane scales one 16-byte piece of T into T' = T diag(beta exp(gamma))
+//   and Tb = T diag(beta);
+//   waves 0-2 transpose K and V (a product with the identity, exact), waves
+//   3-5 form the three nonzero blocks of P;
 //   waves 0-3 form W^T = K^T T'^T by 32 features, waves 4/5 U by 32 columns.
 // Chain and prep meet once per chunk at a workgroup barrier.
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
@@ -389,14 +531,25 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, Lv, 0x00020000);
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc((void *)betab, (short)0, L * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void *)gb, (short)0, gb ? L * 4 : 0, 0x00020000);
+        // T of this head's chunks (written by chunk_t_kernel), bounded by the
+        // chunks that exist. Lane tid < 384 holds one 16-byte piece of the
+        // three nonzero 32x32 blocks: rows 0-31 pieces 0-3, rows 32-63 pieces 0-7.
+        const int nchk = (S + C - 1) / C;
+        const bf16_t *twb = static_cast<const bf16_t *>(p.work) + ((size_t)b * Nv + h) * nchk * tk::CHUNK_ELEMS;
+        const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void *)twb, (short)0, nchunks * tk::CHUNK_ELEMS * 2, 0x00020000);
+        const int trow = tid < 128 ? tid >> 2 : 32 + ((tid - 128) >> 3);
+        const int tpc = tid < 128 ? tid & 3 : (tid - 128) & 7;
+        const int tpoff = tk::piece_offset(trow, tpc);
         // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
-        // waves 0-1 2 x 32 bytes of V, and wave 1 one beta and one g.
-        u32x4_t ra[8];
+        // waves 0-1 2 x 32 bytes of V, wave 1 one beta and one g, and every
+        // lane one piece of T.
+        u32x4_t ra[8], rt;
         uint32_t rb = 0, rg = 0;
         const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
         auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
             constexpr int W = decltype(R)::value;
             const int t0 = cn * C;
+            rt = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + tpoff, 0, 0);
             if constexpr (W >= 2) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -421,10 +574,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             }
         };
-        // 16 consecutive elements (pieces a, b) into k-order: slots 0-3 and
-        // 12-15 stay, slots 4-7 take elements 8-11, slots 8-11 elements 4-7.
-        auto korder_lo = [](u32x4_t a, u32x4_t b) { return u32x4_t{a.x, a.y, b.x, b.y}; };
-        auto korder_hi = [](u32x4_t a, u32x4_t b) { return u32x4_t{a.z, a.w, b.z, b.w}; };
         float *bg = reinterpret_cast<float *>(smem + P_BG);
 
         auto prep = [&](auto R, int cn) __attribute__((always_inline)) {
@@ -466,6 +615,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
                 }
             }
+            const u32x4_t tcur = rt;   // this chunk's piece of T, before the next loads
             issue(R, cn + 1);
             arrive(flags + 0, lane);
             wait_for(flags + 0, 6u * ncall);
@@ -500,101 +650,29 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             };
 
-            if constexpr (W < 2) {
-                // Diagonal block d of A and its inverse.
-                constexpr int d = W;
-                f32x16_t G = zero16();
+            // T' = T diag(beta exp(gamma)) and Tb = T diag(beta) from this
+            // lane's piece of T: slot 8(tpc & 1) + e of column group tpc / 2
+            // holds column 16(tpc / 2) + 4(tpc & 1) + e % 4 + 8(e / 4).
+            {
+                const int i0 = 16 * (tpc >> 1) + 4 * (tpc & 1);
+                const float4 f0 = *reinterpret_cast<const float4 *>(fv + i0), f1 = *reinterpret_cast<const float4 *>(fv + i0 + 8);
+                const float4 b0 = *reinterpret_cast<const float4 *>(bg + i0), b1 = *reinterpret_cast<const float4 *>(bg + i0 + 8);
+                const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                const uint32_t tw4[4] = {tcur.x, tcur.y, tcur.z, tcur.w};
+                bf16x8_t tp, tq;
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8_t a = ld8(set, S_W + sw256(32 * d + c32, 2 * ks + hh));
-                    G = mfma32(a, a, G);
+                for (int e = 0; e < 8; ++e) {
+                    const float t = (e & 1) ? bf16_hi(tw4[e >> 1]) : bf16_lo(tw4[e >> 1]);
+                    tp[e] = (__bf16)(t * fe[e]);
+                    tq[e] = (__bf16)(t * be[e]);
                 }
-                float br[16], gr[16];
-                rows4(bg, 32 * d, br);
-                rows4(gv, 32 * d, gr);
-                const float bc = bg[32 * d + c32], gc = gv[32 * d + c32];
-                // N = D(-A_dd), Nt = D(-A_dd^T), R = D((I - A_dd)^T). At each
-                // position only one of A_dd, A_dd^T can be nonzero (G = K K^T is
-                // symmetric), so one exponential serves both.
-                f32x16_t N, Nt, R;
+                st8(smem, P_TP + sw128(trow, tpc), tp);
+                st8(smem, P_TB + sw128(trow, tpc), tq);
+            }
+            if constexpr (W < 3) {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int rl = drow(q, hh);
-                    const bool below = c32 < rl;
-                    const float dg = gr[q] - gc;
-                    const float a = -__builtin_amdgcn_exp2f(below ? dg : -dg) * (below ? br[q] : bc) * G[q];
-                    N[q] = below ? a : 0.f;
-                    Nt[q] = rl < c32 ? a : 0.f;
-                    R[q] = rl == c32 ? 1.f : Nt[q];
-                }
-                // R_{k+1}^T = R_k^T + (N^(2^k))^T R_k^T, powers by squaring.
-                f32x16_t M = prod(Nt, N, zero16()), Mt = prod(N, Nt, zero16());   // N^2
-                R = prod(M, R, R);
-                f32x16_t M2 = prod(Mt, M, zero16()), M2t = prod(M, Mt, zero16());  // N^4
-                R = prod(M2, R, R);
-                M = prod(M2t, M2, zero16()); Mt = prod(M2, M2t, zero16());       // N^8
-                R = prod(M, R, R);
-                M2 = prod(Mt, M, zero16());                                       // N^16
-                R = prod(M2, R, R);                                               // D(T_dd^T)
-                // T' = T diag(beta exp(gamma)), Tb = T diag(beta), block (d, d).
-                float fp[16];
-                rows4(fv, 32 * d, fp);
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    bf16x8_t tp, tq;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        tp[e] = (__bf16)(R[8 * s + e] * fp[8 * s + e]);
-                        tq[e] = (__bf16)(R[8 * s + e] * br[8 * s + e]);
-                    }
-                    st8(smem, P_TP + sw128(32 * d + c32, 2 * (2 * d + s) + hh), tp);
-                    st8(smem, P_TB + sw128(32 * d + c32, 2 * (2 * d + s) + hh), tq);
-                }
-                if constexpr (d == 1) {
-                    // Z = -(T_11 A_10)^T = -A_10^T T_11^T.
-                    wait_for(flags + 1, ncall);
-                    const bf16x8_t a0 = ld8(smem, P_A10 + lane * 16), a1 = ld8(smem, P_A10 + 1024 + lane * 16);
-                    f32x16_t Z = mfma32(a0, op8(R, 0), zero16());
-                    Z = mfma32(a1, op8(R, 1), Z);
-                    Z = -Z;
-                    st8(smem, P_Z + lane * 16, op8(Z, 0));
-                    st8(smem, P_Z + 1024 + lane * 16, op8(Z, 1));
-                    arrive(flags + 2, lane);
-                } else {
-                    // T_10^T = T_00^T Z; D(T_00) from D(T_00^T) and the identity.
-                    f32x16_t T0 = mfma32(op8(R, 0), eye[0], zero16());
-                    T0 = mfma32(op8(R, 1), eye[1], T0);
-                    wait_for(flags + 2, ncall);
-                    const bf16x8_t z0 = ld8(smem, P_Z + lane * 16), z1 = ld8(smem, P_Z + 1024 + lane * 16);
-                    f32x16_t T10 = mfma32(op8(T0, 0), z0, zero16());
-                    T10 = mfma32(op8(T0, 1), z1, T10);
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        bf16x8_t tp, tq;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            tp[e] = (__bf16)(T10[8 * s + e] * fp[8 * s + e]);
-                            tq[e] = (__bf16)(T10[8 * s + e] * br[8 * s + e]);
-                        }
-                        st8(smem, P_TP + sw128(32 + c32, 2 * s + hh), tp);
-                        st8(smem, P_TB + sw128(32 + c32, 2 * s + hh), tq);
-                    }
-                }
-            } else if constexpr (W == 2) {
-                // A_10: rows 32-63 of A against columns 0-31 (no mask needed).
-                f32x16_t G = zero16();
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-                    G = mfma32(ld8(set, S_W + sw256(32 + c32, 2 * ks + hh)), ld8(set, S_W + sw256(c32, 2 * ks + hh)), G);
-                const float gi = gv[c32];
-                float br[16], gr[16];
-                rows4(bg, 32, br);
-                rows4(gv, 32, gr);
-#pragma unroll
-                for (int q = 0; q < 16; ++q) G[q] *= br[q] * __builtin_amdgcn_exp2f(gr[q] - gi);
-                st8(smem, P_A10 + lane * 16, op8(G, 0));
-                st8(smem, P_A10 + 1024 + lane * 16, op8(G, 1));
-                arrive(flags + 1, lane);
+                for (int j = 0; j < 4; ++j) transpose(4 * W + j);
             } else {
                 // P block (tokens r in block rbq, keys i in block ibq), written as rows r.
                 constexpr int rbq = W == 3 ? 0 : 1, ibq = W == 5 ? 1 : 0;
@@ -614,10 +692,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
-            }
-            if constexpr (W >= 2) {
-#pragma unroll
-                for (int j = 0; j < 3; ++j) transpose(3 * (W - 2) + j);
             }
             // T', Tb, K^T, V^T complete; K and V rows no longer read.
             arrive(flags + 3, lane);
@@ -799,12 +873,29 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkParams p)
     for (int e = nchunks * C * D + tid; e < Sl * D; e += 256) ob[e] = 0.f;
 }
 
+int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, int S)
+{
+    if (dtype == 1 && Dk == mk::DK && Dv == mk::DV && C == mk::C)
+        return (int64_t)B * Nv * ((S + mk::C - 1) / mk::C) * tk::CHUNK_ELEMS * 2;
+    return 0;
+}
+
 hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, hipStream_t s, bool *supported)
 {
     *supported = true;
     ChunkParams pc = p;
     if (dtype == 1) {
         if (Dk == mk::DK && Dv == mk::DV && C == mk::C) {
+            // T of every chunk first, then the pass over the chunks.
+            int nchk = (p.S + mk::C - 1) / mk::C;
+            int tunits = p.B * p.Nv * nchk;
+            if (tunits > 0) {
+                void *targs[] = {&pc, &nchk, &tunits};
+                const hipError_t e = hipLaunchKernel((const void *)chunk_t_kernel,
+                                                     dim3((tunits + tk::WAVES - 1) / tk::WAVES), dim3(64 * tk::WAVES),
+                                                     targs, 0, s);
+                if (e != hipSuccess) return e;
+            }
             const int units = p.B * p.Nv * mk::NT;
             const int nwg = (units + 7) / 8 * 8;
             int u = units;

@@ -25,9 +25,13 @@ struct ChunkParams {
     const int32_t *lens;
     void *out;
     void *fin;
+    void *work;        // caller's workspace (per-chunk T blocks of the matrix-core path)
     float scale;
     int32_t B, Nk, Nv, S;
 };
+
+// Bytes of workspace the chunk launcher needs for these sizes (0: none).
+int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, int S);
 
 // Launchers: return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
 hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported);

@@ -135,16 +135,26 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  *                              initial state when L_b == 0). final_state MAY
  *                              alias initial_state (same pointer).
  *   scale_value                multiplies every output
+ *   workspace, workspace_bytes device scratch owned by the caller, at least
+ *                              gdr_chunk_workspace_size(a) bytes, 16-byte
+ *                              aligned (may be NULL when that size is 0). Its
+ *                              contents on entry do not matter and on return
+ *                              are unspecified; calls that share a workspace
+ *                              must be ordered on one stream.
  * Inputs at positions t >= L_b are never read.
  * The result equals the token-by-token recurrence up to rounding; the state
  * is carried in float32 between chunks.
- * Supported: bf16 with Dk = Dv = 128 and chunk_size 64 (matrix-core path);
- *   f32 with Dk = Dv in {16, 32} and chunk_size in {16, 32, 64}, or
- *   Dk = Dv = 64 and chunk_size in {16, 32}.
- * Errors: GDR_ERR_NULL if a, q, k, v, beta, out or final_state is NULL
- *   (when B > 0); GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1,
- *   Nv % Nk != 0 or chunk_size < 1; GDR_ERR_DTYPE; GDR_ERR_UNSUPPORTED;
- *   GDR_ERR_LAUNCH. B == 0 is a no-op.
+ * Supported: bf16 with Dk = Dv = 128 and chunk_size 64 (matrix-core path,
+ *   which first forms (I + A)^-1 of every chunk in the workspace:
+ *   B * Nv * ceil(S / 64) * 8192 bytes); f32 with Dk = Dv in {16, 32} and
+ *   chunk_size in {16, 32, 64}, or Dk = Dv = 64 and chunk_size in {16, 32}
+ *   (no workspace).
+ * Errors: GDR_ERR_NULL if a, q, k, v, beta, out or final_state is NULL, or
+ *   workspace is NULL while a workspace is needed (when B > 0);
+ *   GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1, Nv % Nk != 0,
+ *   chunk_size < 1 or workspace_bytes is below the needed size;
+ *   GDR_ERR_DTYPE; GDR_ERR_UNSUPPORTED (also for a misaligned pointer or
+ *   S * D * 4 beyond 2^31 - 1); GDR_ERR_LAUNCH. B == 0 is a no-op.
  */
 typedef struct {
     int32_t dtype;
@@ -157,9 +167,15 @@ typedef struct {
     float scale_value;
     void *out;
     void *final_state;
+    void *workspace;
+    int64_t workspace_bytes;
 } gdr_chunk_args;
 
 GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);
+
+/* Bytes of workspace gdr_chunk needs for these arguments (0 if none; reads
+ * dtype, B, Nv, S, Dk, Dv and chunk_size only); -1 if a is NULL. */
+GDR_API int64_t gdr_chunk_workspace_size(const gdr_chunk_args *a);
 
 /* Static, NUL-terminated description of a status code. */
 GDR_API const char *gdr_status_string(gdr_status s);
@@ -167,7 +183,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 1
+#define GDR_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = re.findall(r"GDR_API\s+[\w\s\*]+?\b(gdr_\w+)\s*\(", open(HEADER).read())
-    assert set(names) == {"gdr_decode", "gdr_chunk", "gdr_status_string", "gdr_abi_version"}
+    assert set(names) == {"gdr_decode", "gdr_chunk", "gdr_chunk_workspace_size", "gdr_status_string",
+                          "gdr_abi_version"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", gbuild.LIB], capture_output=True, text=True).stdout
@@ -75,7 +76,8 @@ def _dec(**kw):
 def _chk(**kw):
     a = dict(dtype=gdr.GDR_BF16, B=2, Nk=2, Nv=4, S=100, Dk=128, Dv=128, chunk_size=64,
              q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, initial_state=None,
-             actual_seq_lengths=None, scale_value=1.0, out=FAKE, final_state=FAKE)
+             actual_seq_lengths=None, scale_value=1.0, out=FAKE, final_state=FAKE,
+             workspace=FAKE, workspace_bytes=1 << 40)
     a.update(kw)
     return gdr.ChunkArgs(**a)
 
@@ -118,7 +120,11 @@ def test_decode_validation(lib, kw, code):
     (dict(dtype=gdr.GDR_F32, Dk=128, Dv=128), gdr.GDR_ERR_UNSUPPORTED),
     (dict(dtype=gdr.GDR_F32, Dk=64, Dv=64, chunk_size=64), gdr.GDR_ERR_UNSUPPORTED),
     (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
-    (dict(B=0, q=None, out=None), gdr.GDR_OK),
+    (dict(workspace=None), gdr.GDR_ERR_NULL),
+    (dict(workspace_bytes=2 * 4 * 2 * 8192 - 1), gdr.GDR_ERR_SHAPE),
+    (dict(workspace=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(S=1 << 23), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(B=0, q=None, out=None, workspace=None), gdr.GDR_OK),
 ])
 def test_chunk_validation(lib, kw, code):
     a = _chk(**kw)
@@ -147,3 +153,13 @@ def test_binding_maps_status_to_exceptions(lib):
         with pytest.raises(RuntimeError):
             gdr._check(code, "x")
     gdr._check(gdr.GDR_OK, "x")
+
+
+def test_chunk_workspace_size(lib):
+    # The matrix-core path needs 8 KB per (sequence, value head, chunk of 64);
+    # the float32 path needs none.
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk())) == 2 * 4 * 2 * 8192
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=128))) == 2 * 4 * 2 * 8192
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=0))) == 0
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F32, Dk=32, Dv=32, chunk_size=32))) == 0
+    assert lib.gdr_chunk_workspace_size(None) == -1

@@ -145,9 +145,10 @@ def test_decode_repeated_calls_advance_the_state():
     assert max_err(to_f64(pool), p_ref) <= 2e-2
 
 
-# One-token steps of bf16 128 x 128 heads take the persistent, software-pipelined
-# kernel (each wavefront walks many 32-column tiles with two register sets);
-# these cases exercise its tile walk, its skipped tiles and both gate variants.
+# One-token steps of bf16 128 x 128 heads take the workgroup-per-head kernel:
+# 256 persistent workgroups walk the heads with the next head's loads in
+# flight. These cases exercise the walk (fewer and many more heads than
+# workgroups, ragged tails), skipped heads and both gate variants.
 @pytest.mark.parametrize("gk", [None, (-0.5, -0.001)])
 def test_single_token_skipped_tiles_and_gates(gk):
     # lengths 0/1 and accepted counts 0..2 (0 and 2 are out of range for S = 1);
@@ -167,8 +168,8 @@ def test_single_token_skipped_tiles_and_gates(gk):
     _check_decode(c, out, pool)
 
 
-def test_single_token_many_tiles_per_wave():
-    # 97 * 32 * 4 = 12416 tiles: about six per wavefront, with a ragged tail.
+def test_single_token_many_heads_per_workgroup():
+    # 97 * 32 = 3104 heads: twelve or thirteen per workgroup.
     c = synth.decode_case(B=97, Nk=8, Nv=32, S=1, Dk=128, Dv=128, slots=128, base=4343)
     out, pool = run_decode(c)
     _check_decode(c, out, pool)
@@ -181,7 +182,41 @@ def test_single_token_without_g_and_n_acc():
 
 
 def test_single_token_one_head():
-    # Four tiles in total: fewer tiles than wavefronts.
+    # One head: a single workgroup.
     c = synth.decode_case(B=1, Nk=1, Nv=1, S=1, Dk=128, Dv=128, slots=3, base=4545)
+    out, pool = run_decode(c)
+    _check_decode(c, out, pool)
+
+
+@pytest.mark.parametrize("S,gk", [(2, (-0.5, -0.001)), (3, None), (4, (-0.3, -0.01))])
+def test_multi_token_many_heads_and_skips(S, gk):
+    # 41 * 16 = 656 heads; lengths 0..S+1 (clamped to S), accepted counts
+    # 0..S+1 (0 and S+1 skip the sequence), NaN in every input past a
+    # sequence's length.
+    B, slots = 41, 48
+    rng = np.random.default_rng(5000 + S)
+    lens = rng.integers(0, S + 2, B).astype(np.int32)
+    n_acc = rng.integers(0, S + 2, B).astype(np.int32)
+    idx = np.repeat(rng.permutation(slots)[:B].astype(np.int32), S)
+    c = synth.decode_case(B=B, Nk=4, Nv=16, S=S, Dk=128, Dv=128, slots=slots, gk=gk, lens=lens,
+                          n_acc=n_acc, idx=idx, base=5100 + S, poison_pad=True)
+    say(f"multi token S={S}: skipped {int((c.valid_lengths() == 0).sum())} by length, gk={gk is not None}")
+    out, pool = run_decode(c)
+    assert bool(torch.isfinite(out.float()).all())
+    _check_decode(c, out, pool)
+
+
+def test_multi_token_slot_patterns():
+    # Slots repeated and alternating within a sequence: a token stores the
+    # state unless the next token writes the same slot, so slot a of
+    # [a, b, b, a] ends with the state after the last token, and b with the
+    # state after the third.
+    S = 4
+    pats = [[0, 0, 0, 0], [1, 2, 2, 1], [3, 4, 5, 6], [7, 7, 8, 8], [9, 10, 10, 10], [11, 12, 11, 12]]
+    B = len(pats)
+    idx = np.asarray(pats, dtype=np.int32).reshape(-1)
+    c = synth.decode_case(B=B, Nk=2, Nv=8, S=S, Dk=128, Dv=128, slots=13, gk=(-0.5, -0.001),
+                          lens=np.full(B, S, np.int32), n_acc=np.array([1, 4, 2, 3, 1, 2], np.int32),
+                          idx=idx, base=5200)
     out, pool = run_decode(c)
     _check_decode(c, out, pool)
