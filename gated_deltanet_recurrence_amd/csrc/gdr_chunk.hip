@@ -233,7 +233,7 @@ __device__ __forceinline__ f32x16_t diag_inverse_t(const f32x16_t &G, const floa
     return prod(M2, R, R);
 }
 
-__global__ __launch_bounds__(64 * tk::WAVES) void chunk_t_kernel(ChunkParams p, int nchk, int units)
+__global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_t_kernel(ChunkParams p, int nchk, int units)
 {
     using namespace mk;
     // A few floats per wave: beta and gamma log2(e) of the chunk's tokens.
@@ -318,6 +318,9 @@ __global__ __launch_bounds__(64 * tk::WAVES) void chunk_t_kernel(ChunkParams p, 
 #pragma unroll
     for (int s = 0; s < 2; ++s) put(1, s, op8(R1, s));
     f32x16_t Z = -prod(G10, R1, zero16());
+    // The two inverses run one after the other (G_00 is held back until T_11
+    // is done): overlapped, they would double the registers in use.
+    asm volatile("" : "+v"(G0) : "v"(Z[0]));
     // T_00, then T_10^T = T_00^T Z with D(T_00) from D(T_00^T) and the identity.
     float br0[16], gr0[16];
     rows4(bg, 0, br0);
@@ -414,11 +417,19 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         const __amdgpu_buffer_rsrc_t orsrc =
             __builtin_amdgcn_make_buffer_rsrc(ob, (short)0, (S * DV - col0) * 2, 0x00020000);
         f32x16_t st[4];              // st[f][q] = S[32f + drow(q)][32cw + c32]
+        {
+            // All 64 loads in flight at once: a buffer resource of size 0
+            // when there is no initial state reads zeros, with no branch.
+            const __amdgpu_buffer_rsrc_t irs =
+                __builtin_amdgcn_make_buffer_rsrc((void *)ib, (short)0, ib ? (DK * DV - col0) * 2 : 0, 0x00020000);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+            for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                st[f][q] = ib ? to_f32(ib[(size_t)(32 * f + drow(q, hh)) * DV + 32 * cw + c32]) : 0.f;
+                for (int q = 0; q < 16; ++q)
+                    st[f][q] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                                   irs, ((32 * f + drow(q, hh)) * DV + 32 * cw + c32) * 2, 0, 0)
+                                               << 16);
+        }
         if (nchunks > 0) lds_barrier();   // operand set of chunk 0 is ready
         for (int c = 0; c < nchunks; ++c) {
             const unsigned char *set = smem + (c & 1) * SET_BYTES;
