@@ -90,6 +90,12 @@ __device__ __forceinline__ f32x16_t prod(const f32x16_t &dxt, const f32x16_t &dy
 // groups, so operand reads and result writes are free of bank conflicts.
 __device__ __forceinline__ int sw256(int r, int u) { return (r << 8) + ((u ^ (r & 15)) << 4); }
 __device__ __forceinline__ int sw128(int r, int u) { return (r << 7) + ((u ^ ((r >> 1) & 7)) << 4); }
+// Swizzles of the tiles that are also read transposed (ldT below), whose
+// reads touch 4 consecutive rows x 4 consecutive pieces: consecutive rows
+// are sent to different 64-byte bank groups, while any 16 consecutive rows
+// (256-byte rows) still fall on 16 different piece positions.
+__device__ __forceinline__ int sw256t(int r, int u) { return (r << 8) + ((u ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 4); }
+__device__ __forceinline__ int sw128t(int r, int u) { return (r << 7) + ((u ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))) << 4); }
 
 __device__ __forceinline__ bf16x8_t ld8(const unsigned char *base, int off)
 {
@@ -98,6 +104,33 @@ __device__ __forceinline__ bf16x8_t ld8(const unsigned char *base, int off)
 __device__ __forceinline__ void st8(unsigned char *base, int off, bf16x8_t v)
 {
     *reinterpret_cast<bf16x8_t *>(base + off) = v;
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4_t *lds_i16x4_ptr;
+
+// Operand of k-step ks for a product that contracts over the ROWS of a
+// row-major bf16 tile kept with k-order column pieces (row pitch 256 or 128
+// bytes, swizzled by sw256t / sw128t): lane l takes column 32cb + (l & 31) and
+// rows 16ks + 4(l >> 5) + {0..3, 8..11} (k-order), i.e. the left operand of
+// the tile's transpose or its right operand. Two LDS transpose reads
+// (ds_read_b64_tr_b16): inside each 16-lane group, result lane i gets element
+// i % 4 of the 4 elements named by source lanes 4j + i / 4 (j = 0..3), so
+// source lane m names row T(m / 4) and columns c + 4(m % 4) .. + 3.
+template <int PITCH>
+__device__ __forceinline__ bf16x8_t ldT(const unsigned char *base, int cb, int ks, int lane)
+{
+    const int g = lane >> 4, m = lane & 15;
+    const int row = 16 * ks + 4 * (g >> 1) + (m >> 2);
+    const int c0 = 32 * cb + 16 * (g & 1) + 4 * (m & 3);
+    const int piece = 2 * (c0 >> 4) + ((c0 >> 2) & 1);
+    const int half = 8 * ((c0 >> 3) & 1);
+    const int o1 = (PITCH == 256 ? sw256t(row, piece) : sw128t(row, piece)) + half;
+    const int o2 = (PITCH == 256 ? sw256t(row + 8, piece) : sw128t(row + 8, piece)) + half;
+    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + o1));
+    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + o2));
+    return __builtin_bit_cast(bf16x8_t, i16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
 }
 
 namespace mk {
@@ -111,14 +144,14 @@ constexpr int NTHR = 512;      // 6 prep + 2 chain wavefronts
 // Operand set of one chunk (double-buffered: the chain consumes chunk c while
 // the prep waves build chunk c + 1). Byte offsets within a set:
 constexpr int S_Q = 0;         // Q rows, features in k-order             [64][256 B]
-constexpr int S_KT = 16384;    // K^T rows (features), tokens in k-order  [128][128 B]
-constexpr int S_W = 32768;     // -W rows, features in k-order            [64][256 B]; K rows while staging
+constexpr int S_KT = 16384;    // K rows, features in k-order             [64][256 B] (read transposed)
+constexpr int S_W = 32768;     // -W rows, features in k-order            [64][256 B]
 constexpr int S_P = 49152;     // P rows, tokens in k-order               [64][128 B]
-constexpr int S_U = 57344;     // U in result-register order, bf16       [2][2][2][64][16 B]; V rows while staging
+constexpr int S_U = 57344;     // U in result-register order, bf16       [2][2][2][64][16 B]
 constexpr int S_VEC = 65536;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64], exp(gamma_C)
 constexpr int SET_BYTES = 66560;
 // Prep-only buffers.
-constexpr int P_VT = 2 * SET_BYTES;  // V^T rows (value columns), tokens in k-order [64][128 B]
+constexpr int P_VT = 2 * SET_BYTES;  // V rows, columns in k-order [64][128 B] (read transposed)
 constexpr int P_TP = P_VT + 8192;    // T diag(beta exp(gamma)) rows, k-order     [64][128 B]
 constexpr int P_TB = P_TP + 8192;    // T diag(beta) rows, k-order                [64][128 B]
 constexpr int P_BG = P_TB + 8192;    // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
@@ -357,9 +390,11 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 //   stage K, Q, V and this chunk's T (loaded one chunk earlier) in k-order;
 //   every lane scales one 16-byte piece of T into T' = T diag(beta exp(gamma))
 //   and Tb = T diag(beta);
-//   waves 0-2 transpose K and V (a product with the identity, exact), waves
-//   3-5 form the three nonzero blocks of P;
-//   waves 0-3 form W^T = K^T T'^T by 32 features, waves 4/5 U by 32 columns.
+//   waves 2-4 form the three nonzero blocks of P;
+//   waves 0, 1, 4, 5 form W^T = K^T T'^T by 32 features, waves 2/3 U by 32
+//   columns (waves 2 and 3 share their SIMDs with the chain waves).
+// Products that contract over tokens read K and V through LDS transpose
+// reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
@@ -513,7 +548,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             for (int f = 0; f < 4; ++f)
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2)
-                    st[f] = mfma32(ld8(set, S_KT + sw128(32 * f + c32, 2 * k2 + hh)), vnb[k2], st[f]);
+                    st[f] = mfma32(ldT<256>(set + S_KT, f, k2, lane), vnb[k2], st[f]);
             lds_barrier();
         }
 #pragma unroll
@@ -523,13 +558,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 fb[(size_t)(32 * f + drow(q, hh)) * DV + 32 * cw + c32] = from_f32<bf16_t>(st[f][q]);
     } else {
         // ------------------------------- prep ------------------------------
-        // Identity as a right operand in k-order (exact transposes).
-        bf16x8_t eye[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
 
         // Inputs are read through buffer resources bounded by the sequence's
         // valid length: rows past it come back as zeros from the hardware
@@ -597,8 +625,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
-                    *reinterpret_cast<u32x4_t *>(set + S_W + sw256(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
-                    *reinterpret_cast<u32x4_t *>(set + S_W + sw256(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
                     *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp)) = korder_lo(ra[4 + 2 * m], ra[5 + 2 * m]);
                     *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp + 1)) = korder_hi(ra[4 + 2 * m], ra[5 + 2 * m]);
                 }
@@ -606,8 +634,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
-                    *reinterpret_cast<u32x4_t *>(set + S_U + sw128(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
-                    *reinterpret_cast<u32x4_t *>(set + S_U + sw128(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(smem + P_VT + sw128t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(smem + P_VT + sw128t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
                 }
                 if constexpr (W == 1) {
                     // Per-token factors of chunk cn (lane t = token t): gamma is the
@@ -642,25 +670,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             };
 
-            // Transposes by a product with the identity: job j < 8 is the
-            // K block (tokens 32(j&1), features 32(j>>1)), else the V block
-            // (tokens 32(j&1), columns 32((j-8)>>1)).
-            auto transpose = [&](int j) __attribute__((always_inline)) {
-                const int tb = j & 1, xb = (j & 7) >> 1;
-                f32x16_t d = zero16();
-                if (j < 8) {
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) d = mfma32(ld8(set, S_W + sw256(32 * tb + c32, 2 * (2 * xb + s) + hh)), eye[s], d);
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) st8(set, S_KT + sw128(32 * xb + c32, 2 * (2 * tb + s) + hh), op8(d, s));
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) d = mfma32(ld8(set, S_U + sw128(32 * tb + c32, 2 * (2 * xb + s) + hh)), eye[s], d);
-#pragma unroll
-                    for (int s = 0; s < 2; ++s) st8(smem, P_VT + sw128(32 * xb + c32, 2 * (2 * tb + s) + hh), op8(d, s));
-                }
-            };
-
             // T' = T diag(beta exp(gamma)) and Tb = T diag(beta) from this
             // lane's piece of T: slot 8(tpc & 1) + e of column group tpc / 2
             // holds column 16(tpc / 2) + 4(tpc & 1) + e % 4 + 8(e / 4).
@@ -681,16 +690,16 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 st8(smem, P_TP + sw128(trow, tpc), tp);
                 st8(smem, P_TB + sw128(trow, tpc), tq);
             }
-            if constexpr (W < 3) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) transpose(4 * W + j);
-            } else {
+            // T' and Tb of this lane are written. The P blocks need neither, so
+            // waves 2-4 form them while the other lanes' pieces land.
+            arrive(flags + 3, lane);
+            if constexpr (W == 2 || W == 3 || W == 4) {
                 // P block (tokens r in block rbq, keys i in block ibq), written as rows r.
-                constexpr int rbq = W == 3 ? 0 : 1, ibq = W == 5 ? 1 : 0;
+                constexpr int rbq = W == 2 ? 0 : 1, ibq = W == 4 ? 1 : 0;
                 f32x16_t G = zero16();
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks)
-                    G = mfma32(ld8(set, S_W + sw256(32 * ibq + c32, 2 * ks + hh)),
+                    G = mfma32(ld8(set, S_KT + sw256t(32 * ibq + c32, 2 * ks + hh)),
                                ld8(set, S_Q + sw256(32 * rbq + c32, 2 * ks + hh)), G);
                 const int r = 32 * rbq + c32;
                 const float gq = gv[r];
@@ -704,16 +713,15 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
             }
-            // T', Tb, K^T, V^T complete; K and V rows no longer read.
-            arrive(flags + 3, lane);
+            // T' and Tb complete.
             wait_for(flags + 3, 6u * ncall);
 
-            if constexpr (W < 4) {
-                // -W^T = -(K^T T'^T), features [32W, 32W + 32), written as -W rows.
-                constexpr int fbk = W;
+            if constexpr (W != 2 && W != 3) {
+                // -W^T = -(K^T T'^T), features [32 fbk, 32 fbk + 32), written as -W rows.
+                constexpr int fbk = W < 2 ? W : W - 2;
                 bf16x8_t ak[4];
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ld8(set, S_KT + sw128(32 * fbk + c32, 2 * k2 + hh));
+                for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ldT<256>(set + S_KT, fbk, k2, lane);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     f32x16_t d = zero16();
@@ -726,10 +734,10 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             } else {
                 // U = Tb V for value columns [32vb, 32vb + 32), kept in result order.
-                constexpr int vbk = W - 4;
+                constexpr int vbk = W - 2;
                 bf16x8_t bv[4];
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ld8(smem, P_VT + sw128(32 * vbk + c32, 2 * k2 + hh));
+                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<128>(smem + P_VT, vbk, k2, lane);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     f32x16_t d = zero16();
