@@ -152,9 +152,7 @@ constexpr int S_VEC = 65536;   // scale exp(gamma_t) (0 past the length) [64], e
 constexpr int SET_BYTES = 66560;
 // Prep-only buffers.
 constexpr int P_VT = 2 * SET_BYTES;  // V rows, columns in k-order [64][128 B] (read transposed)
-constexpr int P_TP = P_VT + 8192;    // T diag(beta exp(gamma)) rows, k-order     [64][128 B]
-constexpr int P_TB = P_TP + 8192;    // T diag(beta) rows, k-order                [64][128 B]
-constexpr int P_BG = P_TB + 8192;    // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
+constexpr int P_BG = P_VT + 8192;    // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
 constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
 constexpr int LDS_BYTES = P_FLAG + 64;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -225,13 +223,6 @@ __device__ __forceinline__ void wait_for(uint32_t *f, uint32_t target)
 namespace tk {
 constexpr int WAVES = 4;                  // independent wavefronts per workgroup
 constexpr int CHUNK_ELEMS = 64 * 64;      // workspace elements per chunk
-// Byte offset in a chunk's T of piece `piece` (k-order, 0-7) of row r (0-63).
-__device__ __forceinline__ int piece_offset(int r, int piece)
-{
-    const int j = r < 32 ? 0 : (piece >= 4 ? 1 : 2);
-    const int s = (piece & 3) >> 1, hh = piece & 1;
-    return ((2 * j + s) * 64 + (r & 31) + 32 * hh) * 16;
-}
 }  // namespace tk
 
 // D((I + A_dd)^-1 ^T) for one 32x32 diagonal block, from its Gram block G
@@ -387,12 +378,12 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 // and run these three products for chunk c; their operands never leave
 // registers except W, Q, P, K^T and U, read from the chunk's operand set.
 // Prep waves (0-5) build the operand set of chunk c + 1 meanwhile:
-//   stage K, Q, V and this chunk's T (loaded one chunk earlier) in k-order;
-//   every lane scales one 16-byte piece of T into T' = T diag(beta exp(gamma))
-//   and Tb = T diag(beta);
-//   waves 2-4 form the three nonzero blocks of P;
-//   waves 0, 1, 4, 5 form W^T = K^T T'^T by 32 features, waves 2/3 U by 32
-//   columns (waves 2 and 3 share their SIMDs with the chain waves).
+//   stage K, Q and V in k-order;
+//   waves 0, 1, 4 form the three nonzero blocks of P;
+//   waves 0, 1, 4, 5 form W^T = K^T T'^T by 32 features, waves 2/3 U = Tb V
+//   by 32 columns (waves 2 and 3 share their SIMDs with the chain waves),
+//   with T' = T diag(beta exp(gamma)) and Tb = T diag(beta) scaled in
+//   registers from T's operands, loaded one chunk ahead in register order.
 // Products that contract over tokens read K and V through LDS transpose
 // reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
@@ -570,25 +561,31 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, Lv, 0x00020000);
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc((void *)betab, (short)0, L * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void *)gb, (short)0, gb ? L * 4 : 0, 0x00020000);
-        // T of this head's chunks (written by chunk_t_kernel), bounded by the
-        // chunks that exist. Lane tid < 384 holds one 16-byte piece of the
-        // three nonzero 32x32 blocks: rows 0-31 pieces 0-3, rows 32-63 pieces 0-7.
+        // T of this head's chunks (written by chunk_t_kernel in result-register
+        // order), bounded by the chunks that exist. The W and U products take
+        // their T operands straight from there: operand n of a lane is block j,
+        // k-step s = (T_00, 0), (T_00, 1), (T_10, 0), (T_10, 1), (T_11, 0),
+        // (T_11, 1) for n = 0..5, i.e. row block rb and token k-step k2 =
+        // (0, 0), (0, 1), (1, 0), (1, 1), (1, 2), (1, 3).
         const int nchk = (S + C - 1) / C;
         const bf16_t *twb = static_cast<const bf16_t *>(p.work) + ((size_t)b * Nv + h) * nchk * tk::CHUNK_ELEMS;
         const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void *)twb, (short)0, nchunks * tk::CHUNK_ELEMS * 2, 0x00020000);
-        const int trow = tid < 128 ? tid >> 2 : 32 + ((tid - 128) >> 3);
-        const int tpc = tid < 128 ? tid & 3 : (tid - 128) & 7;
-        const int tpoff = tk::piece_offset(trow, tpc);
         // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
         // waves 0-1 2 x 32 bytes of V, wave 1 one beta and one g, and every
-        // lane one piece of T.
-        u32x4_t ra[8], rt;
+        // wave the six T operands of its W or U product.
+        u32x4_t ra[8], rt[6];
         uint32_t rb = 0, rg = 0;
         const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
         auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
             constexpr int W = decltype(R)::value;
             const int t0 = cn * C;
-            rt = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + tpoff, 0, 0);
+            {
+                constexpr int jb[6] = {0, 0, 2, 2, 1, 1}, sb[6] = {0, 1, 0, 1, 0, 1};
+#pragma unroll
+                for (int n = 0; n < 6; ++n)
+                    rt[n] = __builtin_amdgcn_raw_buffer_load_b128(
+                        trs, cn * tk::CHUNK_ELEMS * 2 + ((2 * jb[n] + sb[n]) * 64 + lane) * 16, 0, 0);
+            }
             if constexpr (W >= 2) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -654,7 +651,9 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
                 }
             }
-            const u32x4_t tcur = rt;   // this chunk's piece of T, before the next loads
+            u32x4_t tcur[6];   // this chunk's T operands, before the next loads
+#pragma unroll
+            for (int n = 0; n < 6; ++n) tcur[n] = rt[n];
             issue(R, cn + 1);
             arrive(flags + 0, lane);
             wait_for(flags + 0, 6u * ncall);
@@ -670,32 +669,23 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             };
 
-            // T' = T diag(beta exp(gamma)) and Tb = T diag(beta) from this
-            // lane's piece of T: slot 8(tpc & 1) + e of column group tpc / 2
-            // holds column 16(tpc / 2) + 4(tpc & 1) + e % 4 + 8(e / 4).
-            {
-                const int i0 = 16 * (tpc >> 1) + 4 * (tpc & 1);
-                const float4 f0 = *reinterpret_cast<const float4 *>(fv + i0), f1 = *reinterpret_cast<const float4 *>(fv + i0 + 8);
-                const float4 b0 = *reinterpret_cast<const float4 *>(bg + i0), b1 = *reinterpret_cast<const float4 *>(bg + i0 + 8);
+            // T operand n scaled by the per-token factors fac of its columns,
+            // tokens 16 k2 + 4hh + {0..3, 8..11} of its k-step k2: T' = T
+            // diag(beta exp(gamma)) for W, Tb = T diag(beta) for U.
+            auto tscaled = [&](int n, const float *fac) __attribute__((always_inline)) {
+                constexpr int k2s[6] = {0, 1, 0, 1, 2, 3};
+                const int i0 = 16 * k2s[n] + 4 * hh;
+                const float4 f0 = *reinterpret_cast<const float4 *>(fac + i0), f1 = *reinterpret_cast<const float4 *>(fac + i0 + 8);
                 const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                const float be[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-                const uint32_t tw4[4] = {tcur.x, tcur.y, tcur.z, tcur.w};
-                bf16x8_t tp, tq;
+                const uint32_t w4[4] = {tcur[n].x, tcur[n].y, tcur[n].z, tcur[n].w};
+                bf16x8_t r;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float t = (e & 1) ? bf16_hi(tw4[e >> 1]) : bf16_lo(tw4[e >> 1]);
-                    tp[e] = (__bf16)(t * fe[e]);
-                    tq[e] = (__bf16)(t * be[e]);
-                }
-                st8(smem, P_TP + sw128(trow, tpc), tp);
-                st8(smem, P_TB + sw128(trow, tpc), tq);
-            }
-            // T' and Tb of this lane are written. The P blocks need neither, so
-            // waves 2-4 form them while the other lanes' pieces land.
-            arrive(flags + 3, lane);
-            if constexpr (W == 2 || W == 3 || W == 4) {
+                for (int e = 0; e < 8; ++e) r[e] = (__bf16)(((e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1])) * fe[e]);
+                return r;
+            };
+            if constexpr (W == 0 || W == 1 || W == 4) {
                 // P block (tokens r in block rbq, keys i in block ibq), written as rows r.
-                constexpr int rbq = W == 2 ? 0 : 1, ibq = W == 4 ? 1 : 0;
+                constexpr int rbq = W == 0 ? 0 : 1, ibq = W == 4 ? 1 : 0;
                 f32x16_t G = zero16();
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks)
@@ -713,9 +703,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
             }
-            // T' and Tb complete.
-            wait_for(flags + 3, 6u * ncall);
-
             if constexpr (W != 2 && W != 3) {
                 // -W^T = -(K^T T'^T), features [32 fbk, 32 fbk + 32), written as -W rows.
                 constexpr int fbk = W < 2 ? W : W - 2;
@@ -727,7 +714,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     f32x16_t d = zero16();
 #pragma unroll
                     for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        d = mfma32(ak[k2], ld8(smem, P_TP + sw128(32 * rb + c32, 2 * k2 + hh)), d);
+                        d = mfma32(ak[k2], tscaled(rb == 0 ? k2 : 2 + k2, fv), d);
                     d = -d;
 #pragma unroll
                     for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8(d, s));
@@ -743,7 +730,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     f32x16_t d = zero16();
 #pragma unroll
                     for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        d = mfma32(ld8(smem, P_TB + sw128(32 * rb + c32, 2 * k2 + hh)), bv[k2], d);
+                        d = mfma32(tscaled(rb == 0 ? k2 : 2 + k2, bg), bv[k2], d);
 #pragma unroll
                     for (int q = 0; q < 2; ++q) st8(set, S_U + ((vbk * 2 + rb) * 2 + q) * 1024 + lane * 16, op8(d, q));
                 }
