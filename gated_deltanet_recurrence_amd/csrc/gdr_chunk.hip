@@ -133,6 +133,26 @@ __device__ __forceinline__ bf16x8_t ldT(const unsigned char *base, int cb, int k
     return __builtin_bit_cast(bf16x8_t, i16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
 }
 
+// Left operand n (0-5) of a product with T diag(fac), from a chunk's T kept as
+// chunk_t_kernel writes it (block j, k-step s in result-register order). The
+// nonzero (row block, token k-step) pairs of T are n = (0,0), (0,1), (1,0),
+// (1,1), (1,2), (1,3), held as (j, s) = (0,0), (0,1), (2,0), (2,1), (1,0),
+// (1,1) (j: 0 = T_00, 1 = T_11, 2 = T_10); the lane's elements e are tokens
+// 16 k2 + 4hh + (e & 3) + 8(e >> 2).
+__device__ __forceinline__ bf16x8_t t_operand(const unsigned char *tbase, int n, const float *fac, int lane)
+{
+    const int j = n < 2 ? 0 : (n < 4 ? 2 : 1), s = n & 1, k2 = n < 2 ? n : n - 2;
+    const u32x4_t t4 = *reinterpret_cast<const u32x4_t *>(tbase + ((2 * j + s) * 64 + lane) * 16);
+    const int i0 = 16 * k2 + 4 * (lane >> 5);
+    const float4 f0 = *reinterpret_cast<const float4 *>(fac + i0), f1 = *reinterpret_cast<const float4 *>(fac + i0 + 8);
+    const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    const uint32_t w4[4] = {t4.x, t4.y, t4.z, t4.w};
+    bf16x8_t r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(((e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1])) * fe[e]);
+    return r;
+}
+
 namespace mk {
 constexpr int C = 64;          // chunk length
 constexpr int DK = 128;        // key head size
@@ -147,12 +167,13 @@ constexpr int S_Q = 0;         // Q rows, features in k-order             [64][2
 constexpr int S_KT = 16384;    // K rows, features in k-order             [64][256 B] (read transposed)
 constexpr int S_W = 32768;     // -W rows, features in k-order            [64][256 B]
 constexpr int S_P = 49152;     // P rows, tokens in k-order               [64][128 B]
-constexpr int S_U = 57344;     // U in result-register order, bf16       [2][2][2][64][16 B]
-constexpr int S_VEC = 65536;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64], exp(gamma_C)
-constexpr int SET_BYTES = 66560;
+constexpr int S_VT = 57344;    // V rows, columns in k-order              [64][128 B] (read transposed)
+constexpr int S_T = 65536;     // T as written by chunk_t_kernel          [6][64][16 B]
+constexpr int S_VEC = 71680;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64],
+                               // exp(gamma_C) [1], beta from float 192 [64]
+constexpr int SET_BYTES = 72704;
 // Prep-only buffers.
-constexpr int P_VT = 2 * SET_BYTES;  // V rows, columns in k-order [64][128 B] (read transposed)
-constexpr int P_BG = P_VT + 8192;    // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
+constexpr int P_BG = 2 * SET_BYTES;  // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
 constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
 constexpr int LDS_BYTES = P_FLAG + 64;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -375,15 +396,16 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 //   S    = exp(gamma_C) S0 + K^T diag(exp(gamma_C - gamma)) Vnew
 //
 // Chain waves (6, 7) each own 32 state columns in float32 result registers
-// and run these three products for chunk c; their operands never leave
-// registers except W, Q, P, K^T and U, read from the chunk's operand set.
+// and, for chunk c, first form U = T diag(beta) V for their columns (it does
+// not depend on the state), then run these three products; their operands
+// never leave registers except W, Q, P, K^T, V and T, read from the chunk's
+// operand set.
 // Prep waves (0-5) build the operand set of chunk c + 1 meanwhile:
-//   stage K, Q and V in k-order;
+//   stage K, Q and V in k-order and T as chunk_t_kernel wrote it;
 //   waves 0, 1, 4 form the three nonzero blocks of P;
-//   waves 0, 1, 4, 5 form W^T = K^T T'^T by 32 features, waves 2/3 U = Tb V
-//   by 32 columns (waves 2 and 3 share their SIMDs with the chain waves),
-//   with T' = T diag(beta exp(gamma)) and Tb = T diag(beta) scaled in
-//   registers from T's operands, loaded one chunk ahead in register order.
+//   waves 2, 3, 5 form W^T = K^T T'^T, T' = T diag(beta exp(gamma)), by 32
+//   features (wave 5 two blocks; waves 2 and 3 share their SIMDs with the
+//   chain waves).
 // Products that contract over tokens read K and V through LDS transpose
 // reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
@@ -465,16 +487,22 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) sop[ks] = op8(st[ks >> 1], ks & 1);
 
-            // Vnew = U - W S0 and S0^T Q^T, one pass over the 128 features.
+            // U = T diag(beta) V for this wave's columns (it does not depend on
+            // the state), then Vnew = U - W S0 and S0^T Q^T, one pass over the
+            // 128 features.
             f32x16_t vn[2], ot[2];
+            {
+                const float *beta = reinterpret_cast<const float *>(set + S_VEC) + 192;
+                bf16x8_t bv[4];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                ot[rb] = zero16();
+                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<128>(set + S_VT, cw, k2, lane);
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const bf16x8_t uu = ld8(set, S_U + ((cw * 2 + rb) * 2 + q) * 1024 + lane * 16);
+                for (int rb = 0; rb < 2; ++rb) {
+                    ot[rb] = zero16();
+                    vn[rb] = zero16();
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) vn[rb][8 * q + e] = (float)uu[e];
+                    for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
+                        vn[rb] = mfma32(t_operand(set + S_T, rb == 0 ? k2 : 2 + k2, beta, lane), bv[k2], vn[rb]);
                 }
             }
 #pragma unroll
@@ -561,31 +589,21 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, Lv, 0x00020000);
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc((void *)betab, (short)0, L * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void *)gb, (short)0, gb ? L * 4 : 0, 0x00020000);
-        // T of this head's chunks (written by chunk_t_kernel in result-register
-        // order), bounded by the chunks that exist. The W and U products take
-        // their T operands straight from there: operand n of a lane is block j,
-        // k-step s = (T_00, 0), (T_00, 1), (T_10, 0), (T_10, 1), (T_11, 0),
-        // (T_11, 1) for n = 0..5, i.e. row block rb and token k-step k2 =
-        // (0, 0), (0, 1), (1, 0), (1, 1), (1, 2), (1, 3).
+        // T of this head's chunks (written by chunk_t_kernel), bounded by the
+        // chunks that exist; a chunk's 6 KB are copied as they are into its
+        // operand set.
         const int nchk = (S + C - 1) / C;
         const bf16_t *twb = static_cast<const bf16_t *>(p.work) + ((size_t)b * Nv + h) * nchk * tk::CHUNK_ELEMS;
         const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void *)twb, (short)0, nchunks * tk::CHUNK_ELEMS * 2, 0x00020000);
         // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
-        // waves 0-1 2 x 32 bytes of V, wave 1 one beta and one g, and every
-        // wave the six T operands of its W or U product.
-        u32x4_t ra[8], rt[6];
+        // waves 0-1 2 x 32 bytes of V and 3 x 16 bytes of T, wave 1 one beta
+        // and one g.
+        u32x4_t ra[8], rt[3];
         uint32_t rb = 0, rg = 0;
         const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
         auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
             constexpr int W = decltype(R)::value;
             const int t0 = cn * C;
-            {
-                constexpr int jb[6] = {0, 0, 2, 2, 1, 1}, sb[6] = {0, 1, 0, 1, 0, 1};
-#pragma unroll
-                for (int n = 0; n < 6; ++n)
-                    rt[n] = __builtin_amdgcn_raw_buffer_load_b128(
-                        trs, cn * tk::CHUNK_ELEMS * 2 + ((2 * jb[n] + sb[n]) * 64 + lane) * 16, 0, 0);
-            }
             if constexpr (W >= 2) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
@@ -604,6 +622,9 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
                     ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16, 0, 0);
                 }
+#pragma unroll
+                for (int n = 0; n < 3; ++n)
+                    rt[n] = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + (ltid + 128 * n) * 16, 0, 0);
                 if constexpr (W == 1) {
                     rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
                     rg = __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
@@ -631,9 +652,11 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
-                    *reinterpret_cast<u32x4_t *>(smem + P_VT + sw128t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
-                    *reinterpret_cast<u32x4_t *>(smem + P_VT + sw128t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                    *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
                 }
+#pragma unroll
+                for (int n = 0; n < 3; ++n) *reinterpret_cast<u32x4_t *>(set + S_T + (ltid + 128 * n) * 16) = rt[n];
                 if constexpr (W == 1) {
                     // Per-token factors of chunk cn (lane t = token t): gamma is the
                     // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
@@ -649,11 +672,9 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     vec[lane] = lane < nv ? p.scale * eg : 0.f;
                     vec[64 + lane] = __builtin_amdgcn_exp2f(gamC2 - gam2);
                     if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
+                    vec[192 + lane] = beta;
                 }
             }
-            u32x4_t tcur[6];   // this chunk's T operands, before the next loads
-#pragma unroll
-            for (int n = 0; n < 6; ++n) tcur[n] = rt[n];
             issue(R, cn + 1);
             arrive(flags + 0, lane);
             wait_for(flags + 0, 6u * ncall);
@@ -669,20 +690,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             };
 
-            // T operand n scaled by the per-token factors fac of its columns,
-            // tokens 16 k2 + 4hh + {0..3, 8..11} of its k-step k2: T' = T
-            // diag(beta exp(gamma)) for W, Tb = T diag(beta) for U.
-            auto tscaled = [&](int n, const float *fac) __attribute__((always_inline)) {
-                constexpr int k2s[6] = {0, 1, 0, 1, 2, 3};
-                const int i0 = 16 * k2s[n] + 4 * hh;
-                const float4 f0 = *reinterpret_cast<const float4 *>(fac + i0), f1 = *reinterpret_cast<const float4 *>(fac + i0 + 8);
-                const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                const uint32_t w4[4] = {tcur[n].x, tcur[n].y, tcur[n].z, tcur[n].w};
-                bf16x8_t r;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) r[e] = (__bf16)(((e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1])) * fe[e]);
-                return r;
-            };
             if constexpr (W == 0 || W == 1 || W == 4) {
                 // P block (tokens r in block rbq, keys i in block ibq), written as rows r.
                 constexpr int rbq = W == 0 ? 0 : 1, ibq = W == 4 ? 1 : 0;
@@ -703,36 +710,32 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
             }
-            if constexpr (W != 2 && W != 3) {
-                // -W^T = -(K^T T'^T), features [32 fbk, 32 fbk + 32), written as -W rows.
-                constexpr int fbk = W < 2 ? W : W - 2;
-                bf16x8_t ak[4];
+            if constexpr (W == 2 || W == 3 || W == 5) {
+                // -W^T = -(K^T T'^T), T' = T diag(beta exp(gamma)), by 32
+                // features, written as -W rows: feature blocks 2 and 3 on waves
+                // 2 and 3, blocks 0 and 1 on wave 5.
+                bf16x8_t tp[6];
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ldT<256>(set + S_KT, fbk, k2, lane);
+                for (int n = 0; n < 6; ++n) tp[n] = t_operand(set + S_T, n, fv, lane);
+                auto wblock = [&](int fbk) __attribute__((always_inline)) {
+                    bf16x8_t ak[4];
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    f32x16_t d = zero16();
+                    for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ldT<256>(set + S_KT, fbk, k2, lane);
 #pragma unroll
-                    for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        d = mfma32(ak[k2], tscaled(rb == 0 ? k2 : 2 + k2, fv), d);
-                    d = -d;
+                    for (int rb = 0; rb < 2; ++rb) {
+                        f32x16_t d = zero16();
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8(d, s));
-                }
-            } else {
-                // U = Tb V for value columns [32vb, 32vb + 32), kept in result order.
-                constexpr int vbk = W - 2;
-                bf16x8_t bv[4];
+                        for (int k2 = 0; k2 < 2 * rb + 2; ++k2) d = mfma32(ak[k2], tp[rb == 0 ? k2 : 2 + k2], d);
+                        d = -d;
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<128>(smem + P_VT, vbk, k2, lane);
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    f32x16_t d = zero16();
-#pragma unroll
-                    for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        d = mfma32(tscaled(rb == 0 ? k2 : 2 + k2, bg), bv[k2], d);
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) st8(set, S_U + ((vbk * 2 + rb) * 2 + q) * 1024 + lane * 16, op8(d, q));
+                        for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8(d, s));
+                    }
+                };
+                if constexpr (W == 5) {
+                    wblock(0);
+                    wblock(1);
+                } else {
+                    wblock(W);
                 }
             }
         };
