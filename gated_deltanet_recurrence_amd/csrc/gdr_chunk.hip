@@ -139,10 +139,15 @@ __device__ __forceinline__ bf16x8_t ldT(const unsigned char *base, int cb, int k
 // (1,1), (1,2), (1,3), held as (j, s) = (0,0), (0,1), (2,0), (2,1), (1,0),
 // (1,1) (j: 0 = T_00, 1 = T_11, 2 = T_10); the lane's elements e are tokens
 // 16 k2 + 4hh + (e & 3) + 8(e >> 2).
+__device__ __forceinline__ int t_operand_offset(int n, int lane)
+{
+    const int j = n < 2 ? 0 : (n < 4 ? 2 : 1), s = n & 1;
+    return ((2 * j + s) * 64 + lane) * 16;
+}
 __device__ __forceinline__ bf16x8_t t_operand(const unsigned char *tbase, int n, const float *fac, int lane)
 {
-    const int j = n < 2 ? 0 : (n < 4 ? 2 : 1), s = n & 1, k2 = n < 2 ? n : n - 2;
-    const u32x4_t t4 = *reinterpret_cast<const u32x4_t *>(tbase + ((2 * j + s) * 64 + lane) * 16);
+    const int k2 = n < 2 ? n : n - 2;
+    const u32x4_t t4 = *reinterpret_cast<const u32x4_t *>(tbase + t_operand_offset(n, lane));
     const int i0 = 16 * k2 + 4 * (lane >> 5);
     const float4 f0 = *reinterpret_cast<const float4 *>(fac + i0), f1 = *reinterpret_cast<const float4 *>(fac + i0 + 8);
     const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
@@ -169,9 +174,9 @@ constexpr int S_W = 32768;     // -W rows, features in k-order            [64][2
 constexpr int S_P = 49152;     // P rows, tokens in k-order               [64][128 B]
 constexpr int S_VT = 57344;    // V rows, columns in k-order              [64][128 B] (read transposed)
 constexpr int S_T = 65536;     // T as written by chunk_t_kernel          [6][64][16 B]
-constexpr int S_VEC = 71680;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64],
-                               // exp(gamma_C) [1], beta from float 192 [64]
-constexpr int SET_BYTES = 72704;
+constexpr int S_TB = 71680;    // T diag(beta) in the same order          [6][64][16 B]
+constexpr int S_VEC = 77824;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64], exp(gamma_C)
+constexpr int SET_BYTES = 78848;
 // Prep-only buffers.
 constexpr int P_BG = 2 * SET_BYTES;  // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
 constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
@@ -396,13 +401,14 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 //   S    = exp(gamma_C) S0 + K^T diag(exp(gamma_C - gamma)) Vnew
 //
 // Chain waves (6, 7) each own 32 state columns in float32 result registers
-// and, for chunk c, first form U = T diag(beta) V for their columns (it does
-// not depend on the state), then run these three products; their operands
-// never leave registers except W, Q, P, K^T, V and T, read from the chunk's
-// operand set.
+// and, for chunk c, also form U = T diag(beta) V for their columns (it does
+// not depend on the state, so it fills gaps in the products' dependency
+// chains); their operands never leave registers except W, Q, P, K^T, V and
+// T diag(beta), read from the chunk's operand set.
 // Prep waves (0-5) build the operand set of chunk c + 1 meanwhile:
 //   stage K, Q and V in k-order and T as chunk_t_kernel wrote it;
-//   waves 0, 1, 4 form the three nonzero blocks of P;
+//   waves 0, 1, 4 form the three nonzero blocks of P, waves 0 and 1 then
+//   T diag(beta);
 //   waves 2, 3, 5 form W^T = K^T T'^T, T' = T diag(beta exp(gamma)), by 32
 //   features (wave 5 two blocks; waves 2 and 3 share their SIMDs with the
 //   chain waves).
@@ -490,9 +496,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             // U = T diag(beta) V for this wave's columns (it does not depend on
             // the state), then Vnew = U - W S0 and S0^T Q^T, one pass over the
             // 128 features.
-            f32x16_t vn[2], ot[2];
+            f32x16_t vn[2], ot[2], uu[2];
             {
-                const float *beta = reinterpret_cast<const float *>(set + S_VEC) + 192;
                 bf16x8_t bv[4];
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<128>(set + S_VT, cw, k2, lane);
@@ -500,22 +505,35 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 for (int rb = 0; rb < 2; ++rb) {
                     ot[rb] = zero16();
                     vn[rb] = zero16();
+                    uu[rb] = zero16();
 #pragma unroll
                     for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        vn[rb] = mfma32(t_operand(set + S_T, rb == 0 ? k2 : 2 + k2, beta, lane), bv[k2], vn[rb]);
+                        uu[rb] = mfma32(ld8(set + S_TB, t_operand_offset(rb == 0 ? k2 : 2 + k2, lane)), bv[k2], uu[rb]);
+                }
+            }
+            {
+                bf16x8_t opd[2][4];
+                auto ldk = [&](int ks, bf16x8_t *o) __attribute__((always_inline)) {
+                    o[0] = ld8(set, S_W + sw256(c32, 2 * ks + hh));
+                    o[1] = ld8(set, S_W + sw256(32 + c32, 2 * ks + hh));
+                    o[2] = ld8(set, S_Q + sw256(c32, 2 * ks + hh));
+                    o[3] = ld8(set, S_Q + sw256(32 + c32, 2 * ks + hh));
+                };
+                ldk(0, opd[0]);
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    if (ks + 1 < 8) ldk(ks + 1, opd[(ks + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    const bf16x8_t *o = opd[ks & 1];
+                    vn[0] = mfma32(o[0], sop[ks], vn[0]);
+                    vn[1] = mfma32(o[1], sop[ks], vn[1]);
+                    ot[0] = mfma32(sop[ks], o[2], ot[0]);
+                    ot[1] = mfma32(sop[ks], o[3], ot[1]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const bf16x8_t aw0 = ld8(set, S_W + sw256(c32, 2 * ks + hh));
-                const bf16x8_t aw1 = ld8(set, S_W + sw256(32 + c32, 2 * ks + hh));
-                const bf16x8_t bq0 = ld8(set, S_Q + sw256(c32, 2 * ks + hh));
-                const bf16x8_t bq1 = ld8(set, S_Q + sw256(32 + c32, 2 * ks + hh));
-                vn[0] = mfma32(aw0, sop[ks], vn[0]);
-                vn[1] = mfma32(aw1, sop[ks], vn[1]);
-                ot[0] = mfma32(sop[ks], bq0, ot[0]);
-                ot[1] = mfma32(sop[ks], bq1, ot[1]);
-            }
+            for (int rb = 0; rb < 2; ++rb) vn[rb] += uu[rb];
             const float *vec = reinterpret_cast<const float *>(set + S_VEC);
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) ot[tb] *= vec[32 * tb + c32];
@@ -598,7 +616,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
         // waves 0-1 2 x 32 bytes of V and 3 x 16 bytes of T, wave 1 one beta
         // and one g.
-        u32x4_t ra[8], rt[3];
+        u32x4_t ra[8], rt[3], traw[3];
         uint32_t rb = 0, rg = 0;
         const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
         auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
@@ -656,7 +674,10 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
                 }
 #pragma unroll
-                for (int n = 0; n < 3; ++n) *reinterpret_cast<u32x4_t *>(set + S_T + (ltid + 128 * n) * 16) = rt[n];
+                for (int n = 0; n < 3; ++n) {
+                    *reinterpret_cast<u32x4_t *>(set + S_T + (ltid + 128 * n) * 16) = rt[n];
+                    traw[n] = rt[n];
+                }
                 if constexpr (W == 1) {
                     // Per-token factors of chunk cn (lane t = token t): gamma is the
                     // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
@@ -672,7 +693,6 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     vec[lane] = lane < nv ? p.scale * eg : 0.f;
                     vec[64 + lane] = __builtin_amdgcn_exp2f(gamC2 - gam2);
                     if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
-                    vec[192 + lane] = beta;
                 }
             }
             issue(R, cn + 1);
@@ -709,6 +729,22 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
+            }
+            if constexpr (W < 2) {
+                // T diag(beta) for the chain's U, from this lane's three pieces
+                // of T (block j = n, k-step s = W: tokens 16 k2 + 4hh + {0..3,
+                // 8..11} with k2 = s, or 2 + s in T_11).
+#pragma unroll
+                for (int n = 0; n < 3; ++n) {
+                    const int i0 = 16 * (n == 1 ? 2 + W : W) + 4 * hh;
+                    const float4 f0 = *reinterpret_cast<const float4 *>(bg + i0), f1 = *reinterpret_cast<const float4 *>(bg + i0 + 8);
+                    const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                    const uint32_t w4[4] = {traw[n].x, traw[n].y, traw[n].z, traw[n].w};
+                    bf16x8_t r;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(((e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1])) * fe[e]);
+                    st8(set, S_TB + (ltid + 128 * n) * 16, r);
+                }
             }
             if constexpr (W == 2 || W == 3 || W == 5) {
                 // -W^T = -(K^T T'^T), T' = T diag(beta exp(gamma)), by 32
