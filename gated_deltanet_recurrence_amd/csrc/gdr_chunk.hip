@@ -286,8 +286,11 @@ __device__ __forceinline__ f32x16_t diag_inverse_t(const f32x16_t &G, const floa
 __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_t_kernel(ChunkParams p, int nchk, int units)
 {
     using namespace mk;
-    // A few floats per wave: beta and gamma log2(e) of the chunk's tokens.
+    // A few floats per wave: beta and gamma log2(e) of the chunk's tokens; and
+    // per wave one 32-row half of the chunk's K, passed through LDS so that
+    // the loads read whole rows.
     __shared__ __align__(16) float bgs[tk::WAVES][128];
+    __shared__ __align__(16) unsigned char kst[tk::WAVES][32 * 256];
     const int Nk = p.Nk, Nv = p.Nv, S = p.S;
     const int rep = Nv / Nk;
     const int lane = threadIdx.x & 63, wl = uniform(threadIdx.x >> 6);
@@ -309,15 +312,24 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     // K operands: row 32d + c32 of the chunk; k-step ks takes features
     // 16ks + 8hh .. + 7. The Gram blocks contract over the features, so any
     // order serves as long as both operands share it. Rows past L read as zeros.
+    // The chunk's 16 KB are read as 16 whole-row loads (1 KB, 4 rows each) and
+    // turned into operands through this wave's LDS half tile, one half at a
+    // time (a wave's LDS accesses complete in order, so no barrier is needed).
     const bf16_t *kb = static_cast<const bf16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, L * DK * 2, 0x00020000);
+    u32x4_t kr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, t0 * DK * 2 + i * 1024 + lane * 16, 0, 0);
     bf16x8_t kf[2][8];
+    unsigned char *kt = kst[wl];
 #pragma unroll
-    for (int d = 0; d < 2; ++d)
+    for (int d = 0; d < 2; ++d) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            kf[d][ks] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         krs, ((t0 + 32 * d + c32) * DK + 16 * ks + 8 * hh) * 2, 0, 0));
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4_t *>(kt + sw256(4 * i + (lane >> 4), lane & 15)) = kr[8 * d + i];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kf[d][ks] = ld8(kt, sw256(c32, 2 * ks + hh));
+    }
     // beta and the in-chunk cumulative log decay (lane t = token t0 + t).
     {
         const size_t vh = (size_t)b * Nv + h;
