@@ -117,6 +117,16 @@ def test_short_and_boundary_lengths(S):
     _check_full(c, out, fin)
 
 
+@pytest.mark.parametrize("gate", [("uniform", -30.0, -3.0), ("uniform", 0.0, 0.0), ("uniform", -1e-4, 0.0)])
+def test_decay_extremes(gate):
+    # decay strong enough that exp(gamma) underflows within a chunk, exactly
+    # none (g = 0 given), and barely any
+    c = synth.prefill_case(B=2, Nk=1, Nv=2, S=200, Dk=128, Dv=128, base=430, gate=gate, init_std=0.05,
+                           lens=[200, 131])
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
 def test_resume_equals_one_shot():
     # prefill of 200 tokens, then 170 more from the returned state, against the
     # oracle's single 370-token pass (the intermediate state is stored in bf16)
