@@ -432,13 +432,18 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     using namespace mk;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    // Workgroup -> unit. Workgroups are dealt round-robin to the 8 XCDs, so
-    // consecutive units (the column tiles and value heads that share one
-    // (b, key head) and therefore the same q/k) go to one XCD and its L2.
-    const int nwg = gridDim.x;
-    const int u = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-    if (u >= units) return;
+    // Workgroup -> unit. Workgroups are dealt round-robin to the 8 XCDs, and
+    // each XCD starts its workgroups in order as its CUs free up. The units of
+    // one (b, key head) — its column tiles and value heads, which share q and
+    // k — form a group kept on one XCD and its L2; consecutive groups go to
+    // consecutive XCDs, so that every XCD gets an even share of long and short
+    // sequences (handing each XCD a contiguous range of sequences instead made
+    // the varlen prefill workload 1.7x longer than its average per XCD).
     const int Nk = p.Nk, Nv = p.Nv, S = p.S;
+    const int G = NT * (Nv / Nk);
+    const int xcd = blockIdx.x % 8, n = blockIdx.x / 8;
+    const int u = (8 * (n / G) + xcd) * G + n % G;
+    if (u >= units) return;
     const int rep = Nv / Nk;
     const int tile = u % NT;
     const int hr = (u / NT) % rep;
@@ -954,7 +959,8 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
                 if (e != hipSuccess) return e;
             }
             const int units = p.B * p.Nv * mk::NT;
-            const int nwg = (units + 7) / 8 * 8;
+            const int G = mk::NT * (p.Nv / p.Nk);   // units of one (b, key head), kept on one XCD
+            const int nwg = (units + 8 * G - 1) / (8 * G) * (8 * G);
             int u = units;
             void *args[] = {&pc, &u};
             // Raise the dynamic-LDS limit once per process (first launch).
