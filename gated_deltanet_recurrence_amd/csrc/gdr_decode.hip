@@ -498,6 +498,191 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
     }
 }
 
+// Decode calls of two to eight tokens per sequence (speculative steps), bf16,
+// Dk = Dv = 128. One workgroup of four wavefronts per (b, h): wave j owns the
+// 32 rows [32j, 32j + 32) of the state, lane l the columns 8 (l % 16) .. + 7
+// of the eight consecutive rows 32j + 8 (l / 16) + i, so that each load or
+// store instruction of a wave moves four whole 256-byte rows. The state stays
+// in float32 registers across the tokens. Per token, with the decayed state
+// S' = D S (D = diag(exp(g) exp(gk_i))):
+//   the column sums S'^T k and S'^T q, over the wave's four lane rows by lane
+//   swaps and over the four waves through LDS (one barrier);
+//   delta = beta (v - S'^T k),  o = scale (S'^T q + delta (k . q));
+//   S <- S' + k delta^T, stored when the next token does not overwrite the
+//   same slot.
+// The next token's inputs are in flight while a token is computed; several
+// workgroups per CU cover each other's barrier waits.
+namespace mt {
+constexpr int DK = 128, DV = 128;
+constexpr int NW = 4;            // waves per head (workgroup size 256)
+constexpr int RW = DK / NW;      // 32 rows per wave
+constexpr int NI = RW / 4;       // 8 rows per lane
+}  // namespace mt
+
+// One token's inputs as a lane holds them.
+struct MTTok {
+    u32x4_t k, q;        // the lane's 8 rows of k and q (bf16)
+    u32x4_t v;           // the lane's 8 columns of v (bf16)
+    u32x4_t gk0, gk1;    // the lane's 8 rows of gk (f32)
+    uint32_t beta, g;    // bf16 in the low half; f32 bits
+    int w;               // the token's write slot
+};
+
+template <bool GK>
+__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mt_kernel(DecodeParams p)
+{
+    using namespace mt;
+    __shared__ float4 red[2][NW][64];
+    __shared__ float redkq[2][NW];
+
+    const int lane = threadIdx.x & 63;
+    const int j = uniform(threadIdx.x >> 6);
+    const int lr = lane >> 4, cg = lane & 15;
+    const int row0 = j * RW + lr * NI;   // the lane's first row
+    const int Nv = p.Nv, S = p.S, rep = p.Nv / p.Nk;
+    const int b = blockIdx.x / Nv, h = blockIdx.x % Nv;
+    const size_t vh = (size_t)b * Nv + h, qk = (size_t)b * p.Nk + h / rep;
+
+    int L = ld_const(p.lens, b);
+    L = L < 0 ? 0 : (L > S ? S : L);
+    const int n = p.nacc ? ld_const(p.nacc, b) : L;
+    int r = -1;
+    if (L > 0 && n >= 1 && n <= S) r = ld_const(p.idx, (size_t)b * S + n - 1);
+    // Output words of this lane in wave 0: columns 8 cg + 2 lr, + 1 of each token.
+    uint32_t *optr = reinterpret_cast<uint32_t *>(static_cast<bf16_t *>(p.out) + vh * S * DV + cg * 8 + lr * 2);
+    if (r < 0 || r >= p.slots) {
+        if (j == 0)
+            for (int t = 0; t < S; ++t) optr[t * (DV / 2)] = 0u;
+        return;
+    }
+
+    // Token inputs through buffer resources bounded by the valid tokens: the
+    // prefetch past the last one reads zeros.
+    const auto krs = brsrc(static_cast<const bf16_t *>(p.k) + qk * S * DK, L * DK * 2);
+    const auto qrs = brsrc(static_cast<const bf16_t *>(p.q) + qk * S * DK, L * DK * 2);
+    const auto vrs = brsrc(static_cast<const bf16_t *>(p.v) + vh * S * DV, L * DV * 2);
+    const auto brs = brsrc(static_cast<const bf16_t *>(p.beta) + vh * S, L * 2);
+    const auto grs = brsrc(p.g ? p.g + vh * S : nullptr, p.g ? L * 4 : 0);
+    const auto gkrs = brsrc(GK ? p.gk + vh * S * DK : nullptr, GK ? L * DK * 4 : 0);
+    auto ld_tok = [&](MTTok &T, int t) __attribute__((always_inline)) {
+        T.k = __builtin_amdgcn_raw_buffer_load_b128(krs, (t * DK + row0) * 2, 0, 0);
+        T.q = __builtin_amdgcn_raw_buffer_load_b128(qrs, (t * DK + row0) * 2, 0, 0);
+        T.v = __builtin_amdgcn_raw_buffer_load_b128(vrs, (t * DV + cg * 8) * 2, 0, 0);
+        if constexpr (GK) {
+            T.gk0 = __builtin_amdgcn_raw_buffer_load_b128(gkrs, (t * DK + row0) * 4, 0, 0);
+            T.gk1 = __builtin_amdgcn_raw_buffer_load_b128(gkrs, (t * DK + row0) * 4 + 16, 0, 0);
+        }
+        T.beta = __builtin_amdgcn_raw_buffer_load_b16(brs, t * 2, 0, 0);
+        T.g = __builtin_amdgcn_raw_buffer_load_b32(grs, t * 4, 0, 0);
+        T.w = ld_const(p.idx, (size_t)b * S + (t < S ? t : S - 1));
+    };
+
+    MTTok cur, nxt;
+    ld_tok(cur, 0);
+    float st[NI][8];
+    {
+        const auto srs = brsrc(static_cast<const bf16_t *>(p.pool) + ((size_t)r * Nv + h) * DK * DV, DK * DV * 2);
+        u32x4_t sw[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) sw[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint32_t w4[4] = {sw[i].x, sw[i].y, sw[i].z, sw[i].w};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st[i][c] = (c & 1) ? bf16_hi(w4[c >> 1]) : bf16_lo(w4[c >> 1]);
+        }
+    }
+    bf16_t *pool = static_cast<bf16_t *>(p.pool);
+    int par = 0;
+    for (int t = 0; t < L; ++t) {
+        ld_tok(nxt, t + 1);
+        const float a = p.g ? __expf(__uint_as_float(cur.g)) : 1.f;
+        float dd[NI], kr[NI], qr[NI];
+        {
+            const uint32_t kw[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w}, qw[4] = {cur.q.x, cur.q.y, cur.q.z, cur.q.w};
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                kr[i] = (i & 1) ? bf16_hi(kw[i >> 1]) : bf16_lo(kw[i >> 1]);
+                qr[i] = (i & 1) ? bf16_hi(qw[i >> 1]) : bf16_lo(qw[i >> 1]);
+            }
+            if constexpr (GK) {
+                const uint32_t gw[8] = {cur.gk0.x, cur.gk0.y, cur.gk0.z, cur.gk0.w, cur.gk1.x, cur.gk1.y, cur.gk1.z, cur.gk1.w};
+#pragma unroll
+                for (int i = 0; i < NI; ++i) dd[i] = a * __expf(__uint_as_float(gw[i]));
+            } else {
+#pragma unroll
+                for (int i = 0; i < NI; ++i) dd[i] = a;
+            }
+        }
+        // Decay, then the partial column sums S'^T k, S'^T q and k . q over
+        // the lane's rows.
+        float kv[8], sq[8], kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { kv[c] = 0.f; sq[c] = 0.f; }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            kq = fmaf(kr[i], qr[i], kq);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                st[i][c] *= dd[i];
+                kv[c] = fmaf(st[i][c], kr[i], kv[c]);
+                sq[c] = fmaf(st[i][c], qr[i], sq[c]);
+            }
+        }
+        // Over the wave: lane row r keeps the totals of columns 8 cg + 2r, + 1.
+        float4 tt;
+        tt.x = rows_reduce4(kv[0], kv[2], kv[4], kv[6]);
+        tt.y = rows_reduce4(kv[1], kv[3], kv[5], kv[7]);
+        tt.z = rows_reduce4(sq[0], sq[2], sq[4], sq[6]);
+        tt.w = rows_reduce4(sq[1], sq[3], sq[5], sq[7]);
+        kq = rows_sum(kq);
+        // Over the workgroup. The two buffers alternate by token: a wave can
+        // write the next token's sums only after every wave has passed this
+        // token's barrier, so after every read of the other buffer.
+        red[par][j][lane] = tt;
+        if (lane == 0) redkq[par][j] = kq;
+        s1_barrier();
+        float4 u = red[par][0][lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) {
+            const float4 x = red[par][w][lane];
+            u.x += x.x; u.y += x.y; u.z += x.z; u.w += x.w;
+        }
+        kq = redkq[par][0] + redkq[par][1] + redkq[par][2] + redkq[par][3];
+        par ^= 1;
+        const float beta = __uint_as_float(cur.beta << 16);
+        const uint32_t vw = lr == 0 ? cur.v.x : lr == 1 ? cur.v.y : lr == 2 ? cur.v.z : cur.v.w;
+        const float d0 = beta * (bf16_lo(vw) - u.x), d1 = beta * (bf16_hi(vw) - u.y);
+        if (j == 0) optr[t * (DV / 2)] = pack_bf16x2(p.scale * fmaf(d0, kq, u.z), p.scale * fmaf(d1, kq, u.w));
+        float e0[4], e1[4], dl[8];
+        rows_gather(d0, e0);
+        rows_gather(d1, e1);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) { dl[2 * q4] = e0[q4]; dl[2 * q4 + 1] = e1[q4]; }
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st[i][c] = fmaf(kr[i], dl[c], st[i][c]);
+        // The state after this token, unless the next token overwrites the
+        // same slot.
+        const int w = cur.w;
+        const bool last = (t == L - 1) || (nxt.w != w);
+        if (last && w >= 0 && w < p.slots) {
+            const auto wrs = brsrc(pool + ((size_t)w * Nv + h) * DK * DV, DK * DV * 2);
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                uint32_t ow[4];
+#pragma unroll
+                for (int c = 0; c < 8; c += 2) ow[c >> 1] = pack_bf16x2(st[i][c], st[i][c + 1]);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, wrs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+            }
+        }
+        cur = nxt;
+    }
+    if (j == 0)
+        for (int t = L; t < S; ++t) optr[t * (DV / 2)] = 0u;
+}
+
 // Tile and vector width per (type, Dk, Dv): 16-byte row segments where the
 // tile holds enough elements, a 32-column tile at most (measured fastest on
 // MI355X among 16/32/64-column tiles and 1-8 waves per workgroup).
@@ -547,6 +732,13 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
         void *args[] = {&pc, &nh};
         const void *fn = p.gk ? (const void *)decode_s1_kernel<true> : (const void *)decode_s1_kernel<false>;
         return hipLaunchKernel(fn, grid, block, args, 0, s);
+    }
+    if (dtype == 1 && p.S >= 2 && Dk == mt::DK && Dv == mt::DV) {
+        *supported = true;
+        DecodeParams pc = p;
+        void *args[] = {&pc};
+        const void *fn = p.gk ? (const void *)decode_mt_kernel<true> : (const void *)decode_mt_kernel<false>;
+        return hipLaunchKernel(fn, dim3((unsigned)(p.B * p.Nv)), dim3(64 * mt::NW), args, 0, s);
     }
     if (dtype == 1) return launch_typed<bf16_t>(Dk, Dv, p, s, supported);
     return launch_typed<float>(Dk, Dv, p, s, supported);
