@@ -529,7 +529,7 @@ struct MTTok {
 };
 
 template <bool GK>
-__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(3))) void decode_mt_kernel(DecodeParams p)
+__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))) void decode_mt_kernel(DecodeParams p)
 {
     using namespace mt;
     __shared__ float4 red[2][NW][64];
@@ -648,7 +648,9 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(3))
             const float4 x = red[par][w][lane];
             u.x += x.x; u.y += x.y; u.z += x.z; u.w += x.w;
         }
-        kq = redkq[par][0] + redkq[par][1] + redkq[par][2] + redkq[par][3];
+        kq = redkq[par][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) kq += redkq[par][w];
         par ^= 1;
         const float beta = __uint_as_float(cur.beta << 16);
         const uint32_t vw = lr == 0 ? cur.v.x : lr == 1 ? cur.v.y : lr == 2 ? cur.v.z : cur.v.w;
