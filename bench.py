@@ -330,7 +330,7 @@ def main():
                                       "lengths and accepted counts U{1..4}, 256-slot pool",
                           "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
                           "state_GBps": state_b / (ms * 1e-3) / 1e9,
-                          "roofline": {"kernel": "decode_kernel<bf16,128,128>", "bound": "hbm", "achieved": gbs,
+                          "roofline": {"kernel": "decode_mt_kernel (multi-token bf16 128x128)", "bound": "hbm", "achieved": gbs,
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                        "traffic": measured_traffic("decode_kernel_speculative_decode.txt", "decode"),
                                        "algorithmic_bytes_per_launch": bytes_call}})
