@@ -37,6 +37,7 @@ class DecodeArgs(ctypes.Structure):
         ("g", _vp), ("gk", _vp), ("state_pool", _vp),
         ("actual_seq_lengths", _vp), ("ssm_state_indices", _vp), ("num_accepted_tokens", _vp),
         ("scale_value", ctypes.c_float), ("out", _vp),
+        ("beta_logits", _vp), ("gate_a", _vp), ("A_log", _vp), ("dt_bias", _vp),
     ]
 
 
@@ -49,6 +50,7 @@ class ChunkArgs(ctypes.Structure):
         ("initial_state", _vp), ("actual_seq_lengths", _vp),
         ("scale_value", ctypes.c_float), ("out", _vp), ("final_state", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_int64),
+        ("beta_logits", _vp), ("gate_a", _vp), ("A_log", _vp), ("dt_bias", _vp),
     ]
 
 
@@ -112,14 +114,42 @@ def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _gates(beta, g, gates, dt, dev, B, Nv, S):
+    """Checks beta/g or the fused gates (beta_logits, a, A_log, dt_bias) and
+    returns the four fused-gate pointers (None when unused)."""
+    if gates is None:
+        if beta is None:
+            raise ValueError("beta is required unless fused gates are given")
+        _need(beta, "beta", dt, dev, (B, Nv, S))
+        _need(g, "g", torch.float32, dev, (B, Nv, S))
+        return None, None, None, None
+    if beta is not None or g is not None:
+        raise ValueError("fused gates replace beta and g: pass beta=None, g=None")
+    try:
+        bl, ga, al, db = gates
+    except (TypeError, ValueError):
+        raise ValueError("gates must be (beta_logits, a, A_log, dt_bias)")
+    _need(bl, "beta_logits", dt, dev, (B, Nv, S))
+    _need(ga, "a", dt, dev, (B, Nv, S))
+    _need(al, "A_log", torch.float32, dev, (Nv,))
+    _need(db, "dt_bias", torch.float32, dev, (Nv,))
+    if bl is None or ga is None or al is None or db is None:
+        raise ValueError("fused gates need all of beta_logits, a, A_log, dt_bias")
+    return _ptr(bl), _ptr(ga), _ptr(al), _ptr(db)
+
+
 def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices, g=None, gk=None,
-               num_accepted_tokens=None, scale_value=1.0, out=None):
+               num_accepted_tokens=None, scale_value=1.0, out=None, gates=None):
     """Recurrent decode; updates state_pool in place. Returns (out, state_pool).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); state_pool
     (slots, Nv, Dk, Dv) — all of one dtype (bfloat16 or float32); g (B, Nv, S)
     and gk (B, Nv, S, Dk) float32 or None; actual_seq_lengths (B,),
     ssm_state_indices (B*S,), num_accepted_tokens (B,) or None — int32.
+    gates: None, or (beta_logits, a, A_log, dt_bias) — logits and a (B, Nv, S)
+    in the dtype, A_log and dt_bias (Nv,) float32 — in place of beta and g
+    (pass beta=None): the kernels form beta = sigmoid(beta_logits) and
+    g = -exp(A_log) * softplus(a + dt_bias).
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
@@ -134,11 +164,10 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     _need(q, "query", dt, dev, (B, Nk, S, Dk))
     _need(k, "key", dt, dev)
     _need(v, "value", dt, dev, (B, Nv, S, Dv))
-    _need(beta, "beta", dt, dev, (B, Nv, S))
+    fused = _gates(beta, g, gates, dt, dev, B, Nv, S)
     if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (Nv, Dk, Dv):
         raise ValueError(f"state has shape {tuple(state_pool.shape)}, expected (slots, {Nv}, {Dk}, {Dv})")
     _need(state_pool, "state", dt, dev)
-    _need(g, "g", torch.float32, dev, (B, Nv, S))
     _need(gk, "gk", torch.float32, dev, (B, Nv, S, Dk))
     _need(actual_seq_lengths, "actual_seq_lengths", torch.int32, dev, (B,))
     _need(ssm_state_indices, "ssm_state_indices", torch.int32, dev)
@@ -149,19 +178,19 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     a = DecodeArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, state_pool.shape[0], ssm_state_indices.numel(),
                    _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(gk), _ptr(state_pool),
                    _ptr(actual_seq_lengths), _ptr(ssm_state_indices), _ptr(num_accepted_tokens),
-                   float(scale_value), _ptr(out))
+                   float(scale_value), _ptr(out), *fused)
     _check(load_library().gdr_decode(ctypes.byref(a), _stream(dev)), "gdr_decode")
     return out, state_pool
 
 
 def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
-              chunk_size=64, out=None, final_state=None):
+              chunk_size=64, out=None, final_state=None, gates=None):
     """Chunked prefill. Returns (out, final_state).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); initial_state
     (B, Nv, Dk, Dv) or None — one dtype; g (B, Nv, S) float32 or None;
     actual_seq_lengths (B,) int32 or None. final_state may be initial_state
-    itself (updated in place).
+    itself (updated in place). gates: as for gdr_decode.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
@@ -176,9 +205,8 @@ def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None
     _need(q, "query", dt, dev, (B, Nk, S, Dk))
     _need(k, "key", dt, dev)
     _need(v, "value", dt, dev, (B, Nv, S, Dv))
-    _need(beta, "beta", dt, dev, (B, Nv, S))
+    fused = _gates(beta, g, gates, dt, dev, B, Nv, S)
     _need(initial_state, "initial_state", dt, dev, (B, Nv, Dk, Dv))
-    _need(g, "g", torch.float32, dev, (B, Nv, S))
     _need(actual_seq_lengths, "actual_seq_lengths", torch.int32, dev, (B,))
     if out is None:
         out = torch.empty((B, Nv, S, Dv), dtype=dt, device=dev)
@@ -188,7 +216,8 @@ def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None
     _need(final_state, "final_state", dt, dev, (B, Nv, Dk, Dv))
     a = ChunkArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, int(chunk_size),
                   _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
-                  _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state))
+                  _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state),
+                  None, 0, *fused)
     lib = load_library()
     ws = chunk_workspace(a, dev)
     _check(lib.gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")

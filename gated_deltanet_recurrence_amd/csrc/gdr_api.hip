@@ -8,6 +8,17 @@ namespace {
 
 bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
+// Either beta (and optionally g), or the fused gates: the logits, a, A_log and
+// dt_bias together, with neither beta nor g.
+gdr_status check_gates(const void *beta, const void *logits, const float *g, const void *ga, const float *A_log,
+                       const float *dt_bias)
+{
+    if (!logits && !ga) return beta ? GDR_OK : GDR_ERR_NULL;
+    if (beta || g) return GDR_ERR_SHAPE;
+    if (!logits || !ga || !A_log || !dt_bias) return GDR_ERR_NULL;
+    return GDR_OK;
+}
+
 gdr_status from_launch(hipError_t e, bool supported)
 {
     if (!supported) return GDR_ERR_UNSUPPORTED;
@@ -42,17 +53,22 @@ gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
         return GDR_ERR_SHAPE;
     if (a->num_state_indices != (int64_t)a->B * a->S) return GDR_ERR_SHAPE;
     if (a->B == 0) return GDR_OK;
-    if (!a->q || !a->k || !a->v || !a->beta || !a->state_pool || !a->out || !a->actual_seq_lengths ||
+    if (!a->q || !a->k || !a->v || !a->state_pool || !a->out || !a->actual_seq_lengths ||
         !a->ssm_state_indices)
         return GDR_ERR_NULL;
+    const gdr_status gs = check_gates(a->beta, a->beta_logits, a->g, a->gate_a, a->A_log, a->dt_bias);
+    if (gs != GDR_OK) return gs;
     if ((int64_t)a->B * a->Nv * 2 > 0x7fffffffLL) return GDR_ERR_UNSUPPORTED;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->state_pool) ||
         !aligned16(a->out) || !aligned16(a->gk))
         return GDR_ERR_UNSUPPORTED;
 
     gdr::DecodeParams p;
-    p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta;
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.beta = a->beta ? a->beta : a->beta_logits;
+    p.beta_logit = a->beta ? 0 : 1;
     p.g = a->g; p.gk = a->gk;
+    p.gate_a = a->gate_a; p.A_log = a->A_log; p.dt_bias = a->dt_bias;
     p.pool = a->state_pool;
     p.lens = a->actual_seq_lengths; p.idx = a->ssm_state_indices; p.nacc = a->num_accepted_tokens;
     p.out = a->out;
@@ -78,7 +94,9 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
         a->chunk_size < 1 || a->Nv % a->Nk != 0)
         return GDR_ERR_SHAPE;
     if (a->B == 0) return GDR_OK;
-    if (!a->q || !a->k || !a->v || !a->beta || !a->out || !a->final_state) return GDR_ERR_NULL;
+    if (!a->q || !a->k || !a->v || !a->out || !a->final_state) return GDR_ERR_NULL;
+    const gdr_status gs = check_gates(a->beta, a->beta_logits, a->g, a->gate_a, a->A_log, a->dt_bias);
+    if (gs != GDR_OK) return gs;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) ||
         !aligned16(a->initial_state) || !aligned16(a->final_state) || !aligned16(a->workspace))
         return GDR_ERR_UNSUPPORTED;
@@ -91,8 +109,11 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     if (need > a->workspace_bytes) return GDR_ERR_SHAPE;
 
     gdr::ChunkParams p;
-    p.q = a->q; p.k = a->k; p.v = a->v; p.beta = a->beta;
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.beta = a->beta ? a->beta : a->beta_logits;
+    p.beta_logit = a->beta ? 0 : 1;
     p.g = a->g;
+    p.gate_a = a->gate_a; p.A_log = a->A_log; p.dt_bias = a->dt_bias;
     p.init = a->initial_state;
     p.lens = a->actual_seq_lengths;
     p.out = a->out;

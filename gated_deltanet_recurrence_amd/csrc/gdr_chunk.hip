@@ -335,12 +335,23 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
         const size_t vh = (size_t)b * Nv + h;
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(static_cast<const bf16_t *>(p.beta) + vh * S), (short)0, L * 2, 0x00020000);
+        // g, or with fused gates the raw input a (bf16).
+        const bool fg = p.gate_a != nullptr;
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.g ? p.g + vh * S : nullptr), (short)0, p.g ? L * 4 : 0, 0x00020000);
+            fg ? (void *)(static_cast<const bf16_t *>(p.gate_a) + vh * S) : (void *)(p.g ? p.g + vh * S : nullptr),
+            (short)0, fg ? L * 2 : (p.g ? L * 4 : 0), 0x00020000);
         const uint32_t rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
-        const uint32_t rg = __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
-        bgs[wl][lane] = __uint_as_float(rb << 16);
-        bgs[wl][64 + lane] = wave_prefix_sum(__uint_as_float(rg)) * 1.44269504088896340736f;
+        const uint32_t rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
+                               : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
+        float beta = __uint_as_float(rb << 16), g = __uint_as_float(rg);
+        if (fg) {
+            // Tokens past the length are identity steps: beta = g = 0.
+            const bool valid = t0 + lane < L;
+            beta = valid ? gate_sigmoid(beta) : 0.f;
+            g = valid ? gate_g(__uint_as_float(rg << 16), p.A_log[h], p.dt_bias[h]) : 0.f;
+        }
+        bgs[wl][lane] = beta;
+        bgs[wl][64 + lane] = wave_prefix_sum(g) * 1.44269504088896340736f;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's own writes, read below
     }
     const float *bg = bgs[wl], *gv = bgs[wl] + 64;
@@ -467,7 +478,10 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     const bf16_t *kb = static_cast<const bf16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
     const bf16_t *vb = static_cast<const bf16_t *>(p.v) + ((size_t)b * Nv + h) * S * DV + col0;
     const bf16_t *betab = static_cast<const bf16_t *>(p.beta) + ((size_t)b * Nv + h) * S;
-    const float *gb = p.g ? p.g + ((size_t)b * Nv + h) * S : nullptr;
+    // g (float32), or with fused gates the raw input a (bf16)
+    const bool fg = p.gate_a != nullptr;
+    const void *gb = fg ? (const void *)(static_cast<const bf16_t *>(p.gate_a) + ((size_t)b * Nv + h) * S)
+                        : (const void *)(p.g ? p.g + ((size_t)b * Nv + h) * S : nullptr);
     bf16_t *ob = static_cast<bf16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV + col0;
     const bf16_t *ib = p.init ? static_cast<const bf16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
     bf16_t *fb = static_cast<bf16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
@@ -623,7 +637,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void *)qb, (short)0, Lk, 0x00020000);
         const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, Lv, 0x00020000);
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc((void *)betab, (short)0, L * 2, 0x00020000);
-        const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc((void *)gb, (short)0, gb ? L * 4 : 0, 0x00020000);
+        const __amdgpu_buffer_rsrc_t grs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)gb, (short)0, gb ? L * (fg ? 2 : 4) : 0, 0x00020000);
         // T of this head's chunks (written by chunk_t_kernel), bounded by the
         // chunks that exist; a chunk's 6 KB are copied as they are into its
         // operand set.
@@ -662,7 +677,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     rt[n] = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + (ltid + 128 * n) * 16, 0, 0);
                 if constexpr (W == 1) {
                     rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
-                    rg = __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
+                    rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
+                            : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
                 }
             }
         };
@@ -699,8 +715,13 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     // Per-token factors of chunk cn (lane t = token t): gamma is the
                     // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
                     const int nv = min(C, L - cn * C);
-                    const float beta = __uint_as_float(rb << 16);
-                    const float gam2 = wave_prefix_sum(__uint_as_float(rg)) * 1.44269504088896340736f;
+                    float beta = __uint_as_float(rb << 16), g = __uint_as_float(rg);
+                    if (fg) {
+                        // Fused gates; tokens past the length are identity steps.
+                        beta = lane < nv ? gate_sigmoid(beta) : 0.f;
+                        g = lane < nv ? gate_g(__uint_as_float(rg << 16), p.A_log[h], p.dt_bias[h]) : 0.f;
+                    }
+                    const float gam2 = wave_prefix_sum(g) * 1.44269504088896340736f;
                     const float gamC2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam2), 63));
                     const float eg = __builtin_amdgcn_exp2f(gam2);
                     bg[lane] = beta;
@@ -848,6 +869,8 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkParams p)
     const float *vb = static_cast<const float *>(p.v) + ((size_t)b * Nv + h) * Sl * D;
     const float *betab = static_cast<const float *>(p.beta) + ((size_t)b * Nv + h) * Sl;
     const float *gb = p.g ? p.g + ((size_t)b * Nv + h) * Sl : nullptr;
+    // fused gates: beta holds the logits, and g comes from a
+    const float *gab = p.gate_a ? static_cast<const float *>(p.gate_a) + ((size_t)b * Nv + h) * Sl : nullptr;
     float *ob = static_cast<float *>(p.out) + ((size_t)b * Nv + h) * Sl * D;
     const float *ib = p.init ? static_cast<const float *>(p.init) + ((size_t)b * Nv + h) * D * D : nullptr;
     float *fb = static_cast<float *>(p.fin) + ((size_t)b * Nv + h) * D * D;
@@ -865,11 +888,11 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkParams p)
             Qc[r * LD + j] = ok ? qb[(size_t)(t0 + r) * D + j] : 0.f;
             Vc[r * LD + j] = ok ? vb[(size_t)(t0 + r) * D + j] : 0.f;
         }
-        if (tid < C) bet[tid] = tid < nval ? betab[t0 + tid] : 0.f;
+        if (tid < C) bet[tid] = tid < nval ? (p.beta_logit ? gate_sigmoid(betab[t0 + tid]) : betab[t0 + tid]) : 0.f;
         if (tid == 0) {
             float a = 0.f;
             for (int r = 0; r < C; ++r) {
-                a += (gb && r < nval) ? gb[t0 + r] : 0.f;
+                if (r < nval) a += gab ? gate_g(gab[t0 + r], p.A_log[h], p.dt_bias[h]) : (gb ? gb[t0 + r] : 0.f);
                 gam[r] = a;
             }
         }

@@ -7,17 +7,23 @@
 namespace gdr {
 
 // Kernel-side view of a decode call (all device pointers; sizes validated on the host).
+// beta points at beta or, when beta_logit is set, at the gate logits b; gate_a
+// (dtype), A_log and dt_bias (float32) are set when g is formed in the kernel.
 struct DecodeParams {
     const void *q, *k, *v, *beta;
     const float *g, *gk;
     void *pool;
     const int32_t *lens, *idx, *nacc;
     void *out;
+    const void *gate_a;
+    const float *A_log, *dt_bias;
     float scale;
     int32_t B, Nk, Nv, S, slots;
+    int32_t beta_logit;
 };
 
 // Kernel-side view of a chunked prefill call.
+// Gates as in DecodeParams.
 struct ChunkParams {
     const void *q, *k, *v, *beta;
     const float *g;
@@ -26,8 +32,11 @@ struct ChunkParams {
     void *out;
     void *fin;
     void *work;        // caller's workspace (per-chunk T blocks of the matrix-core path)
+    const void *gate_a;
+    const float *A_log, *dt_bias;
     float scale;
     int32_t B, Nk, Nv, S;
+    int32_t beta_logit;
 };
 
 // Bytes of workspace the chunk launcher needs for these sizes (0: none).
@@ -58,6 +67,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Fused gates (the Gated DeltaNet blog post's layer code; inferencelayer
+// deltanet.rs, module header and its softplus): beta = sigmoid(b) and
+// g = -exp(A_log) softplus(a + dt_bias), in float32.
+__device__ __forceinline__ float gate_sigmoid(float b) { return 1.f / (1.f + __expf(-b)); }
+// ln(1 + e^x); beyond |x| = 20 one of the two terms is below float32
+// resolution and the result is x or e^x.
+__device__ __forceinline__ float gate_softplus(float x)
+{
+    return x > 20.f ? x : (x < -20.f ? __expf(x) : __logf(1.f + __expf(x)));
+}
+__device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias)
+{
+    return -__expf(A_log) * gate_softplus(a + dt_bias);
+}
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }

@@ -119,10 +119,14 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
         load_run<T, RPL>(k + qkoff, kr);
         load_run<T, RPL>(q + qkoff, qr);
         VecIO<T, VEC>::load(v + (vh * S + t) * DV + col, vv);
-        const float bt = to_f32(beta[vh * S + t]);
+        const float braw = to_f32(beta[vh * S + t]);
+        const float bt = p.beta_logit ? gate_sigmoid(braw) : braw;
 
         // Decay: the whole state by exp(g), row i additionally by exp(gk[i]).
-        const float a = p.g ? __expf(p.g[vh * S + t]) : 1.f;
+        const float a = p.g ? __expf(p.g[vh * S + t])
+                            : (p.gate_a ? __expf(gate_g(to_f32(static_cast<const T *>(p.gate_a)[vh * S + t]), p.A_log[h],
+                                                        p.dt_bias[h]))
+                                        : 1.f);
         if (p.gk) {
             float gkr[RPL];
             load_run<float, RPL>(p.gk + (vh * S + t) * DK + row0, gkr);
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
 #pragma unroll
                 for (int c = 0; c < VEC; ++c) st[i][c] *= f;
             }
-        } else if (p.g) {
+        } else if (p.g || p.gate_a) {
 #pragma unroll
             for (int i = 0; i < RPL; ++i)
 #pragma unroll
@@ -223,8 +227,9 @@ constexpr int GROUPS = GDR_S1_GROUPS; // persistent workgroups
 constexpr int NB = GDR_S1_NB;         // heads whose loads are in flight
 }  // namespace s1
 
-// Scalars of a head, read through the scalar cache ahead of use.
-struct S1Scal { int32_t len, nacc, idx, beta2, g; };
+// Scalars of a head, read through the scalar cache ahead of use: beta (or its
+// logit) and, with fused gates, a as bf16 pairs; A_log and dt_bias of the head.
+struct S1Scal { int32_t len, nacc, idx, beta2, g, alog = 0, dtb = 0; };
 // One head's loads and resolution (r < 0: nothing to do).
 struct S1Head {
     int b, h, r;
@@ -279,7 +284,9 @@ __device__ __forceinline__ void s1_barrier()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool GK>
+// GK: per-key decay gk given. FG: fused gates, beta and g formed in the
+// kernel from the logits and the raw gate input a.
+template <bool GK, bool FG>
 __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, int nheads)
 {
     using namespace s1;
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
     // Optional inputs are read from a valid stand-in address and discarded,
     // so no load sits under a branch.
     const int32_t *nacc_src = p.nacc ? p.nacc : p.lens;
-    const int32_t *g_src = p.g ? reinterpret_cast<const int32_t *>(p.g) : p.lens;
+    const int32_t *g_src = FG ? static_cast<const int32_t *>(p.gate_a) : (p.g ? reinterpret_cast<const int32_t *>(p.g) : p.lens);
     const int32_t *beta_src = static_cast<const int32_t *>(p.beta);
 
     auto scal = [&](int hd) __attribute__((always_inline)) {
@@ -313,7 +320,11 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         c.nacc = ld_const(nacc_src, b);
         c.idx = ld_const(p.idx, b);
         c.beta2 = ld_const(beta_src, vh >> 1);
-        c.g = ld_const(g_src, p.g ? vh : 0);
+        c.g = ld_const(g_src, FG ? vh >> 1 : (p.g ? vh : 0));
+        if constexpr (FG) {
+            c.alog = ld_const(reinterpret_cast<const int32_t *>(p.A_log), h);
+            c.dtb = ld_const(reinterpret_cast<const int32_t *>(p.dt_bias), h);
+        }
         return c;
     };
     // Resolves a head from its scalars and issues all of its loads.
@@ -326,8 +337,12 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         const int n = p.nacc ? c.nacc : L;
         const int r = (hd < nheads && L == 1 && n == 1) ? c.idx : -1;
         H.r = (r >= 0 && r < p.slots) ? r : -1;
-        H.beta = __uint_as_float(((uint32_t)c.beta2 >> (16 * (vh & 1))) << 16);
-        H.g = p.g ? __int_as_float(c.g) : 0.f;
+        const float braw = __uint_as_float(((uint32_t)c.beta2 >> (16 * (vh & 1))) << 16);
+        H.beta = FG ? gate_sigmoid(braw) : braw;
+        if constexpr (FG)
+            H.g = gate_g(__uint_as_float(((uint32_t)c.g >> (16 * (vh & 1))) << 16), __int_as_float(c.alog), __int_as_float(c.dtb));
+        else
+            H.g = p.g ? __int_as_float(c.g) : 0.f;
         const bool on = H.r >= 0;
         const auto srs = brsrc(pool + ((size_t)(on ? H.r : 0) * Nv + H.h) * DK * DV, on ? DK * DV * 2 : 0);
 #pragma unroll
@@ -524,11 +539,11 @@ struct MTTok {
     u32x4_t k, q;        // the lane's 8 rows of k and q (bf16)
     u32x4_t v;           // the lane's 8 columns of v (bf16)
     u32x4_t gk0, gk1;    // the lane's 8 rows of gk (f32)
-    uint32_t beta, g;    // bf16 in the low half; f32 bits
+    uint32_t beta, g;    // bf16 in the low half (beta or its logit; a); g as f32 bits
     int w;               // the token's write slot
 };
 
-template <bool GK>
+template <bool GK, bool FG>
 __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))) void decode_mt_kernel(DecodeParams p)
 {
     using namespace mt;
@@ -562,7 +577,11 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
     const auto qrs = brsrc(static_cast<const bf16_t *>(p.q) + qk * S * DK, L * DK * 2);
     const auto vrs = brsrc(static_cast<const bf16_t *>(p.v) + vh * S * DV, L * DV * 2);
     const auto brs = brsrc(static_cast<const bf16_t *>(p.beta) + vh * S, L * 2);
-    const auto grs = brsrc(p.g ? p.g + vh * S : nullptr, p.g ? L * 4 : 0);
+    // g (float32), or with fused gates the raw a (bf16)
+    const auto grs = FG ? brsrc(static_cast<const bf16_t *>(p.gate_a) + vh * S, L * 2)
+                        : brsrc(p.g ? p.g + vh * S : nullptr, p.g ? L * 4 : 0);
+    const float alog = FG ? __int_as_float(ld_const(reinterpret_cast<const int32_t *>(p.A_log), h)) : 0.f;
+    const float dtb = FG ? __int_as_float(ld_const(reinterpret_cast<const int32_t *>(p.dt_bias), h)) : 0.f;
     const auto gkrs = brsrc(GK ? p.gk + vh * S * DK : nullptr, GK ? L * DK * 4 : 0);
     auto ld_tok = [&](MTTok &T, int t) __attribute__((always_inline)) {
         T.k = __builtin_amdgcn_raw_buffer_load_b128(krs, (t * DK + row0) * 2, 0, 0);
@@ -573,7 +592,10 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
             T.gk1 = __builtin_amdgcn_raw_buffer_load_b128(gkrs, (t * DK + row0) * 4 + 16, 0, 0);
         }
         T.beta = __builtin_amdgcn_raw_buffer_load_b16(brs, t * 2, 0, 0);
-        T.g = __builtin_amdgcn_raw_buffer_load_b32(grs, t * 4, 0, 0);
+        if constexpr (FG)
+            T.g = __builtin_amdgcn_raw_buffer_load_b16(grs, t * 2, 0, 0);
+        else
+            T.g = __builtin_amdgcn_raw_buffer_load_b32(grs, t * 4, 0, 0);
         T.w = ld_const(p.idx, (size_t)b * S + (t < S ? t : S - 1));
     };
 
@@ -596,7 +618,8 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
     int par = 0;
     for (int t = 0; t < L; ++t) {
         ld_tok(nxt, t + 1);
-        const float a = p.g ? __expf(__uint_as_float(cur.g)) : 1.f;
+        const float a = FG ? __expf(gate_g(__uint_as_float(cur.g << 16), alog, dtb))
+                           : (p.g ? __expf(__uint_as_float(cur.g)) : 1.f);
         float dd[NI], kr[NI], qr[NI];
         {
             const uint32_t kw[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w}, qw[4] = {cur.q.x, cur.q.y, cur.q.z, cur.q.w};
@@ -652,7 +675,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
 #pragma unroll
         for (int w = 1; w < NW; ++w) kq += redkq[par][w];
         par ^= 1;
-        const float beta = __uint_as_float(cur.beta << 16);
+        const float beta = FG ? gate_sigmoid(__uint_as_float(cur.beta << 16)) : __uint_as_float(cur.beta << 16);
         const uint32_t vw = lr == 0 ? cur.v.x : lr == 1 ? cur.v.y : lr == 2 ? cur.v.z : cur.v.w;
         const float d0 = beta * (bf16_lo(vw) - u.x), d1 = beta * (bf16_hi(vw) - u.y);
         if (j == 0) optr[t * (DV / 2)] = pack_bf16x2(p.scale * fmaf(d0, kq, u.z), p.scale * fmaf(d1, kq, u.w));
@@ -732,14 +755,16 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
         DecodeParams pc = p;
         int nh = nheads;
         void *args[] = {&pc, &nh};
-        const void *fn = p.gk ? (const void *)decode_s1_kernel<true> : (const void *)decode_s1_kernel<false>;
+        const void *fn = p.gate_a ? (p.gk ? (const void *)decode_s1_kernel<true, true> : (const void *)decode_s1_kernel<false, true>)
+                                  : (p.gk ? (const void *)decode_s1_kernel<true, false> : (const void *)decode_s1_kernel<false, false>);
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
     if (dtype == 1 && p.S >= 2 && Dk == mt::DK && Dv == mt::DV) {
         *supported = true;
         DecodeParams pc = p;
         void *args[] = {&pc};
-        const void *fn = p.gk ? (const void *)decode_mt_kernel<true> : (const void *)decode_mt_kernel<false>;
+        const void *fn = p.gate_a ? (p.gk ? (const void *)decode_mt_kernel<true, true> : (const void *)decode_mt_kernel<false, true>)
+                                  : (p.gk ? (const void *)decode_mt_kernel<true, false> : (const void *)decode_mt_kernel<false, false>);
         return hipLaunchKernel(fn, dim3((unsigned)(p.B * p.Nv)), dim3(64 * mt::NW), args, 0, s);
     }
     if (dtype == 1) return launch_typed<bf16_t>(Dk, Dv, p, s, supported);

@@ -26,6 +26,15 @@
  *    g and gk are always float32. Integers are int32.
  *  - Value head h uses key/query head h / (Nv / Nk): the repeat-interleave
  *    grouping of the blog post's layer code. Nv must be a multiple of Nk.
+ *  - Fused gates (optional, both calls). Instead of beta and g, a caller may
+ *    pass the layer's raw gate inputs, and the kernels form the gates as the
+ *    Gated DeltaNet blog post's layer code and inferencelayer deltanet.rs
+ *    (module header; its DN_STEP / DN_CHUNK kernels) do:
+ *      beta = sigmoid(beta_logits),  g = -exp(A_log[h]) * softplus(gate_a + dt_bias[h])
+ *    beta_logits and gate_a are (B, Nv, S) in dtype; A_log and dt_bias are
+ *    (Nv) float32 per value head. The four come together, in place of beta
+ *    and g (which must then be NULL). The gates are formed in float32 and
+ *    never stored; positions t >= L_b are never read.
  *  - Return codes are produced on the host before anything is enqueued
  *    (except GDR_ERR_LAUNCH, from the launch itself). No value of g or gk is
  *    checked (the operator pages leave their sign unchecked on purpose).
@@ -70,8 +79,10 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  * Tensors (device, row-major):
  *   q, k      (B, Nk, S, Dk)   dtype; callers pass L2-normalised vectors
  *   v         (B, Nv, S, Dv)   dtype
- *   beta      (B, Nv, S)       dtype, write strength in [0, 1]
- *   g         (B, Nv, S)       float32 log decay; NULL means alpha = 1
+ *   beta      (B, Nv, S)       dtype, write strength in [0, 1] (NULL with
+ *                              fused gates)
+ *   g         (B, Nv, S)       float32 log decay; NULL means alpha = 1 (and
+ *                              with fused gates)
  *   gk        (B, Nv, S, Dk)   float32 per-key log decay, or NULL
  *   state_pool (num_slots, Nv, Dk, Dv) dtype — read and UPDATED IN PLACE
  *   actual_seq_lengths (B)     int32; L_b = clamp(value, 0, S)
@@ -92,10 +103,12 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *   Two sequences of one call must not share a slot (the result is undefined).
  *   A call is not idempotent: it advances the pool.
  * Supported: Dk, Dv in {16, 32, 64, 128}; both dtypes.
- * Errors: GDR_ERR_NULL if a is NULL or q, k, v, beta, state_pool, out,
- *   actual_seq_lengths or ssm_state_indices is NULL (when B > 0);
- *   GDR_ERR_SHAPE if B < 0, S outside [1, 8], Nk, Nv, Dk, Dv or num_slots
- *   < 1, Nv % Nk != 0, or num_state_indices != B*S; GDR_ERR_DTYPE;
+ * Errors: GDR_ERR_NULL if a is NULL or q, k, v, state_pool, out,
+ *   actual_seq_lengths or ssm_state_indices is NULL, beta is NULL without
+ *   fused gates, or one of the four fused-gate pointers is given without the
+ *   others (when B > 0); GDR_ERR_SHAPE if B < 0, S outside [1, 8], Nk, Nv,
+ *   Dk, Dv or num_slots < 1, Nv % Nk != 0, num_state_indices != B*S, or beta
+ *   or g is given together with fused gates; GDR_ERR_DTYPE;
  *   GDR_ERR_UNSUPPORTED; GDR_ERR_LAUNCH. B == 0 is a no-op.
  */
 typedef struct {
@@ -111,6 +124,10 @@ typedef struct {
     const int32_t *num_accepted_tokens;
     float scale_value;
     void *out;
+    /* fused gates (see the conventions above), or NULL */
+    const void *beta_logits;
+    const void *gate_a;
+    const float *A_log, *dt_bias;
 } gdr_decode_args;
 
 GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
@@ -126,8 +143,9 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  * Tensors (device, row-major):
  *   q, k      (B, Nk, S, Dk)   dtype
  *   v         (B, Nv, S, Dv)   dtype
- *   beta      (B, Nv, S)       dtype
+ *   beta      (B, Nv, S)       dtype (NULL with fused gates)
  *   g         (B, Nv, S)       float32 log decay, or NULL meaning alpha = 1
+ *                              (NULL with fused gates)
  *   initial_state (B, Nv, Dk, Dv) dtype, or NULL meaning zeros
  *   actual_seq_lengths (B)     int32 or NULL (all S); L_b = clamp(value, 0, S)
  *   out       (B, Nv, S, Dv)   dtype; rows t >= L_b are written as exact zeros
@@ -149,10 +167,12 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  *   B * Nv * ceil(S / 64) * 8192 bytes); f32 with Dk = Dv in {16, 32} and
  *   chunk_size in {16, 32, 64}, or Dk = Dv = 64 and chunk_size in {16, 32}
  *   (no workspace).
- * Errors: GDR_ERR_NULL if a, q, k, v, beta, out or final_state is NULL, or
- *   workspace is NULL while a workspace is needed (when B > 0);
- *   GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1, Nv % Nk != 0,
- *   chunk_size < 1 or workspace_bytes is below the needed size;
+ * Errors: GDR_ERR_NULL if a, q, k, v, out or final_state is NULL, beta is
+ *   NULL without fused gates, one of the four fused-gate pointers is given
+ *   without the others, or workspace is NULL while a workspace is needed
+ *   (when B > 0); GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1,
+ *   Nv % Nk != 0, chunk_size < 1, workspace_bytes is below the needed size,
+ *   or beta or g is given together with fused gates;
  *   GDR_ERR_DTYPE; GDR_ERR_UNSUPPORTED (also for a misaligned pointer or
  *   S * D * 4 beyond 2^31 - 1); GDR_ERR_LAUNCH. B == 0 is a no-op.
  */
@@ -169,6 +189,10 @@ typedef struct {
     void *final_state;
     void *workspace;
     int64_t workspace_bytes;
+    /* fused gates (see the conventions above), or NULL */
+    const void *beta_logits;
+    const void *gate_a;
+    const float *A_log, *dt_bias;
 } gdr_chunk_args;
 
 GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);
@@ -183,7 +207,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 2
+#define GDR_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -181,6 +181,18 @@ def _uniform_gates(base, B, Nv, S, lo, hi):
     return _per_b(base, T_A, B, lambda rng, b: rng.uniform(lo, hi, (Nv, S)).astype(np.float32))
 
 
+def gate_inputs(base, B, Nv, S, dtype):
+    """Raw inputs of the fused gates, drawn from the same streams as the gate
+    recipe above: beta logits b ~ N(0, 1) and a ~ N(0, 1) per token (stored in
+    the I/O dtype), A_log ~ U(-2, 1) and dt_bias ~ U(-1, 1) per value head
+    (float32). Returns (beta_logits, a, A_log, dt_bias)."""
+    logits = _per_b(base, T_B, B, lambda rng, b: _store(rng.standard_normal((Nv, S)), dtype))
+    a = _per_b(base, T_A, B, lambda rng, b: _store(rng.standard_normal((Nv, S)), dtype))
+    a_log = _rng(base, T_ALOG).uniform(-2.0, 1.0, Nv).astype(np.float32)
+    dt_bias = _rng(base, T_DTBIAS).uniform(-1.0, 1.0, Nv).astype(np.float32)
+    return logits, a, a_log, dt_bias
+
+
 def _poison(case: Case):
     """Puts NaN into every input position past each sequence's valid length."""
     L = case.valid_lengths()

@@ -82,6 +82,21 @@ def _chk(**kw):
     return gdr.ChunkArgs(**a)
 
 
+# Fused gates: the logits, a, A_log and dt_bias come together, in place of beta and g.
+_FUSED = dict(beta=None, beta_logits=FAKE, gate_a=FAKE, A_log=FAKE, dt_bias=FAKE)
+_GATE_CASES = [
+    (dict(_FUSED, beta=FAKE), gdr.GDR_ERR_SHAPE),
+    (dict(_FUSED, g=FAKE), gdr.GDR_ERR_SHAPE),
+    (dict(_FUSED, beta_logits=None), gdr.GDR_ERR_NULL),
+    (dict(_FUSED, gate_a=None), gdr.GDR_ERR_NULL),
+    (dict(_FUSED, A_log=None), gdr.GDR_ERR_NULL),
+    (dict(_FUSED, dt_bias=None), gdr.GDR_ERR_NULL),
+    (dict(beta_logits=FAKE), gdr.GDR_ERR_SHAPE),
+    (dict(_FUSED, Dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(_FUSED, B=0, num_state_indices=0, q=None, out=None, workspace=None), gdr.GDR_OK),
+]
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), gdr.GDR_ERR_DTYPE),
     (dict(S=0), gdr.GDR_ERR_SHAPE),
@@ -101,7 +116,8 @@ def _chk(**kw):
     (dict(v=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
     (dict(gk=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, num_state_indices=0, q=None, out=None), gdr.GDR_OK),
-])
+    (dict(beta=None), gdr.GDR_ERR_NULL),
+] + _GATE_CASES)
 def test_decode_validation(lib, kw, code):
     a = _dec(**kw)
     assert lib.gdr_decode(ctypes.byref(a), None) == code
@@ -125,7 +141,8 @@ def test_decode_validation(lib, kw, code):
     (dict(workspace=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
     (dict(S=1 << 23), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, q=None, out=None, workspace=None), gdr.GDR_OK),
-])
+    (dict(beta=None), gdr.GDR_ERR_NULL),
+] + _GATE_CASES)
 def test_chunk_validation(lib, kw, code):
     a = _chk(**kw)
     assert lib.gdr_chunk(ctypes.byref(a), None) == code

@@ -285,3 +285,50 @@ def test_contractive_under_decay_and_bounded_beta():
         peak = max(peak, np.linalg.norm(S))
         assert np.isfinite(S).all()
     assert peak < 20.0
+
+
+# --- fused gates (blog post layer code; deltanet.rs module header) ----------
+
+def test_sigmoid_closed_forms():
+    from oracle.gates import sigmoid
+    assert sigmoid(np.array([0.0]))[0] == 0.5
+    assert abs(sigmoid(np.array([math.log(3.0)]))[0] - 0.75) < 1e-15          # 1 / (1 + 1/3)
+    assert abs(sigmoid(np.array([-math.log(3.0)]))[0] - 0.25) < 1e-15
+    x = np.random.default_rng(5).uniform(-30, 30, 1000)
+    assert np.abs(sigmoid(x) + sigmoid(-x) - 1.0).max() < 1e-15               # symmetry
+    ext = sigmoid(np.array([-800.0, 800.0]))
+    assert ext[0] == 0.0 and ext[1] == 1.0                                      # no overflow, no NaN
+    assert np.all(np.diff(sigmoid(np.sort(x))) >= 0)
+
+
+def test_softplus_closed_forms():
+    from oracle.gates import softplus
+    assert abs(softplus(np.array([0.0]))[0] - math.log(2.0)) < 1e-16
+    assert abs(softplus(np.array([math.log(math.e - 1.0)]))[0] - 1.0) < 1e-15  # ln(1 + e - 1) = 1
+    x = np.random.default_rng(6).uniform(-40, 40, 1000)
+    assert np.abs(softplus(x) - softplus(-x) - x).max() < 1e-12                 # ln((1+e^x)/(1+e^-x)) = x
+    assert abs(softplus(np.array([50.0]))[0] - (50.0 + math.exp(-50.0))) < 1e-12
+    assert abs(softplus(np.array([-50.0]))[0] - math.exp(-50.0)) < 1e-30
+    assert np.all(softplus(x) > 0)
+
+
+def test_gate_closed_forms():
+    from oracle.gates import gates
+    Nv, S = 3, 4
+    A_log = np.array([math.log(2.0), 0.0, -1.0])
+    dt_bias = np.array([0.5, -0.25, 1.0])
+    # a + dt_bias = ln(e - 1) everywhere: softplus = 1, so g = -exp(A_log)
+    a = np.full((1, Nv, S), math.log(math.e - 1.0)) - dt_bias[None, :, None]
+    b = np.zeros((1, Nv, S))
+    beta, g = gates(b, a, A_log, dt_bias)
+    assert beta.shape == g.shape == (1, Nv, S)
+    assert np.all(beta == 0.5)
+    assert np.abs(g - (-np.exp(A_log))[None, :, None]).max() < 1e-15
+    assert abs(g[0, 0, 0] + 2.0) < 1e-15
+    # g < 0, increasing toward 0 as a falls; per-head parameters act per head
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((2, Nv, 64)) * 3
+    _, g = gates(rng.standard_normal((2, Nv, 64)), a, A_log, dt_bias)
+    assert np.all(g < 0)
+    order = np.argsort(a[0, 1])
+    assert np.all(np.diff(g[0, 1][order]) <= 0)
