@@ -82,7 +82,14 @@ def measured_traffic(profile, kind):
 # ---------------------------------------------------------------------------
 # algorithmic work per call
 # ---------------------------------------------------------------------------
-def decode_bytes(c):
+def gate_bytes(c, fused):
+    """Gate bytes per token and value head: beta and g, or with fused gates
+    the beta logits and a (A_log and dt_bias are per call)."""
+    e = esize(c.dtype)
+    return 2 * e if fused else e + (4 if c.g is not None else 0)
+
+
+def decode_bytes(c, fused=False):
     """State read once per active sequence and written once per distinct
     consecutive write slot, plus token inputs, outputs and integers."""
     e = esize(c.dtype)
@@ -102,21 +109,21 @@ def decode_bytes(c):
             writes += int(last and 0 <= w < slots)
         state += hs * (1 + writes)
         tok += int(L[b])
-    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * e + (4 * c.Nv if c.g is not None else 0) \
+    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * gate_bytes(c, fused) \
         + (4 * c.Nv * c.Dk if c.gk is not None else 0)
     out = c.B * c.S * c.Nv * c.Dv * e
-    ints = c.B * 4 * (2 if c.n_acc is not None else 1) + c.B * c.S * 4
+    ints = c.B * 4 * (2 if c.n_acc is not None else 1) + c.B * c.S * 4 + (8 * c.Nv if fused else 0)
     return state, state + tok * per_tok + out + ints, tok
 
 
-def prefill_work(c):
+def prefill_work(c, fused=False):
     """(bytes, flops) per call. Flops per token and value head:
     C(3Dk + 2Dv) + C^2/3 + 6 Dk Dv (triangular products counted at half)."""
     e = esize(c.dtype)
     L = c.valid_lengths()
     T = int(L.sum())
-    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * e + (4 * c.Nv if c.g is not None else 0)
-    out = c.B * c.S * c.Nv * c.Dv * e
+    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * gate_bytes(c, fused)
+    out = c.B * c.S * c.Nv * c.Dv * e + (8 * c.Nv if fused else 0)
     states = c.B * c.Nv * c.Dk * c.Dv * e * ((1 if c.state is not None else 0) + 1)
     C = c.chunk
     f_tok = C * (3 * c.Dk + 2 * c.Dv) + C * C / 3 + 6 * c.Dk * c.Dv
@@ -167,19 +174,28 @@ def time_calls(calls, steps, warmup, use_graph):
     return e0.elapsed_time(e1) / steps, wall, steps
 
 
-def decode_calls(c, copies):
-    """Pre-marshalled gdr_decode calls, one per copy of the pool and inputs."""
+def fused_gate_tensors(c, fused):
+    """Device tensors of the fused gates (beta logits, a, A_log, dt_bias), or
+    None; the plain beta and g are then left out of the call."""
+    return None if fused is None else [dev(x) for x in fused]
+
+
+def decode_calls(c, copies, fused=None):
+    """Pre-marshalled gdr_decode calls, one per copy of the pool and inputs.
+    fused: None, or the fused-gate storage arrays (synth.gate_inputs)."""
     lib = gdr.load_library()
     calls, keep = [], []
     for _ in range(copies):
-        t = dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), beta=dev(c.beta), g=dev(c.g), gk=dev(c.gk),
+        t = dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), beta=None if fused else dev(c.beta),
+                 g=None if fused else dev(c.g), gk=dev(c.gk),
                  pool=dev(c.state), lens=dev(c.lens), idx=dev(c.idx), nacc=dev(c.n_acc))
         t["out"] = torch.empty((c.B, c.Nv, c.S, c.Dv), dtype=t["q"].dtype, device="cuda")
+        t["gates"] = fused_gate_tensors(c, fused)
         p = lambda x: None if x is None else x.data_ptr()
         a = gdr.DecodeArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S,
                            c.Dk, c.Dv, c.state.shape[0], c.idx.size, p(t["q"]), p(t["k"]), p(t["v"]),
                            p(t["beta"]), p(t["g"]), p(t["gk"]), p(t["pool"]), p(t["lens"]), p(t["idx"]),
-                           p(t["nacc"]), c.scale, p(t["out"]))
+                           p(t["nacc"]), c.scale, p(t["out"]), *[p(x) for x in (t["gates"] or [None] * 4)])
         keep.append((t, a))
 
         def call(a=a):
@@ -190,18 +206,20 @@ def decode_calls(c, copies):
     return calls, keep
 
 
-def chunk_calls(c, copies):
+def chunk_calls(c, copies, fused=None):
     lib = gdr.load_library()
     calls, keep = [], []
     for _ in range(copies):
-        t = dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), beta=dev(c.beta), g=dev(c.g), init=dev(c.state),
-                 lens=dev(c.lens))
+        t = dict(q=dev(c.q), k=dev(c.k), v=dev(c.v), beta=None if fused else dev(c.beta),
+                 g=None if fused else dev(c.g), init=dev(c.state), lens=dev(c.lens))
         t["out"] = torch.empty((c.B, c.Nv, c.S, c.Dv), dtype=t["q"].dtype, device="cuda")
         t["fin"] = torch.empty((c.B, c.Nv, c.Dk, c.Dv), dtype=t["q"].dtype, device="cuda")
+        t["gates"] = fused_gate_tensors(c, fused)
         p = lambda x: None if x is None else x.data_ptr()
         a = gdr.ChunkArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S, c.Dk,
                           c.Dv, c.chunk, p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["g"]),
-                          p(t["init"]), p(t["lens"]), c.scale, p(t["out"]), p(t["fin"]))
+                          p(t["init"]), p(t["lens"]), c.scale, p(t["out"]), p(t["fin"]), None, 0,
+                          *[p(x) for x in (t["gates"] or [None] * 4)])
         t["ws"] = gdr.chunk_workspace(a, torch.device("cuda"))
         keep.append((t, a))
 
@@ -266,7 +284,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="decode pool copies rotated per step")
     ap.add_argument("--varlen", action="store_true", help="also time the varlen prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen"], default=None)
+    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused"], default=None)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -335,6 +353,43 @@ def main():
                                        "traffic": measured_traffic("decode_kernel_speculative_decode.txt", "decode"),
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "fused"):
+        # The decode step and chunked prefill workloads with fused gates: the
+        # kernels form beta and g from the beta logits and a (bf16) and the
+        # per-head A_log and dt_bias, in place of reading beta (bf16) and g (f32).
+        log("decode step workload, fused gates")
+        c = synth.config(2)
+        state_b, bytes_call, tok = decode_bytes(c, fused=True)
+        calls, keep = decode_calls(c, args.copies, fused=synth.gate_inputs(202, c.B, c.Nv, c.S, c.dtype))
+        ms, wall, _ = time_calls(calls, args.steps, args.warmup, use_graph)
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        secondary.append({"workload": "decode step, fused gates: B=64 Nk=16 Nv=32 S=1 Dk=Dv=128 bf16, beta logits "
+                                      "and a in bf16, A_log and dt_bias per head",
+                          "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "state_GBps": state_b / (ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "decode_s1_kernel (fused gates)", "bound": "hbm", "achieved": gbs,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                       "traffic": None, "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls
+        torch.cuda.empty_cache()
+        log("chunked prefill workload, fused gates")
+        c = synth.config(4)
+        bytes_call, flops, tok = prefill_work(c, fused=True)
+        calls, keep = chunk_calls(c, 2, fused=synth.gate_inputs(404, c.B, c.Nv, c.S, c.dtype))
+        ms, wall, _ = time_calls(calls, max(10, args.steps // 8), max(2, args.warmup // 8), use_graph)
+        tf = flops / (ms * 1e-3) / 1e12
+        secondary.append({"workload": "chunked prefill, fused gates: B=4 S=4096 Nk=16 Nv=32 Dk=Dv=128 bf16, "
+                                      "initial state, C=64, beta logits and a in bf16",
+                          "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel (fused gates)", "bound": "mfma",
+                                       "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                                       "algorithmic_flops_per_launch": flops,
+                                       "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls, c
         torch.cuda.empty_cache()
 
     prefill_sets = []
