@@ -38,6 +38,7 @@ class DecodeArgs(ctypes.Structure):
         ("actual_seq_lengths", _vp), ("ssm_state_indices", _vp), ("num_accepted_tokens", _vp),
         ("scale_value", ctypes.c_float), ("out", _vp),
         ("beta_logits", _vp), ("gate_a", _vp), ("A_log", _vp), ("dt_bias", _vp),
+        ("use_qk_l2norm", ctypes.c_int32),
     ]
 
 
@@ -51,6 +52,7 @@ class ChunkArgs(ctypes.Structure):
         ("scale_value", ctypes.c_float), ("out", _vp), ("final_state", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_int64),
         ("beta_logits", _vp), ("gate_a", _vp), ("A_log", _vp), ("dt_bias", _vp),
+        ("use_qk_l2norm", ctypes.c_int32),
     ]
 
 
@@ -139,7 +141,7 @@ def _gates(beta, g, gates, dt, dev, B, Nv, S):
 
 
 def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices, g=None, gk=None,
-               num_accepted_tokens=None, scale_value=1.0, out=None, gates=None):
+               num_accepted_tokens=None, scale_value=1.0, out=None, gates=None, use_qk_l2norm=False):
     """Recurrent decode; updates state_pool in place. Returns (out, state_pool).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); state_pool
@@ -149,7 +151,8 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     gates: None, or (beta_logits, a, A_log, dt_bias) — logits and a (B, Nv, S)
     in the dtype, A_log and dt_bias (Nv,) float32 — in place of beta and g
     (pass beta=None): the kernels form beta = sigmoid(beta_logits) and
-    g = -exp(A_log) * softplus(a + dt_bias).
+    g = -exp(A_log) * softplus(a + dt_bias). use_qk_l2norm: the kernels
+    normalise q and k (x / sqrt(sum(x^2) + 1e-6)) before use.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
@@ -178,19 +181,19 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     a = DecodeArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, state_pool.shape[0], ssm_state_indices.numel(),
                    _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(gk), _ptr(state_pool),
                    _ptr(actual_seq_lengths), _ptr(ssm_state_indices), _ptr(num_accepted_tokens),
-                   float(scale_value), _ptr(out), *fused)
+                   float(scale_value), _ptr(out), *fused, int(bool(use_qk_l2norm)))
     _check(load_library().gdr_decode(ctypes.byref(a), _stream(dev)), "gdr_decode")
     return out, state_pool
 
 
 def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
-              chunk_size=64, out=None, final_state=None, gates=None):
+              chunk_size=64, out=None, final_state=None, gates=None, use_qk_l2norm=False):
     """Chunked prefill. Returns (out, final_state).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); initial_state
     (B, Nv, Dk, Dv) or None — one dtype; g (B, Nv, S) float32 or None;
     actual_seq_lengths (B,) int32 or None. final_state may be initial_state
-    itself (updated in place). gates: as for gdr_decode.
+    itself (updated in place). gates, use_qk_l2norm: as for gdr_decode.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
@@ -217,7 +220,7 @@ def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None
     a = ChunkArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, int(chunk_size),
                   _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
                   _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state),
-                  None, 0, *fused)
+                  None, 0, *fused, int(bool(use_qk_l2norm)))
     lib = load_library()
     ws = chunk_workspace(a, dev)
     _check(lib.gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")

@@ -69,6 +69,7 @@ gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
     p.beta_logit = a->beta ? 0 : 1;
     p.g = a->g; p.gk = a->gk;
     p.gate_a = a->gate_a; p.A_log = a->A_log; p.dt_bias = a->dt_bias;
+    p.qk_norm = a->use_qk_l2norm != 0;
     p.pool = a->state_pool;
     p.lens = a->actual_seq_lengths; p.idx = a->ssm_state_indices; p.nacc = a->num_accepted_tokens;
     p.out = a->out;
@@ -114,6 +115,7 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     p.beta_logit = a->beta ? 0 : 1;
     p.g = a->g;
     p.gate_a = a->gate_a; p.A_log = a->A_log; p.dt_bias = a->dt_bias;
+    p.qk_norm = a->use_qk_l2norm != 0;
     p.init = a->initial_state;
     p.lens = a->actual_seq_lengths;
     p.out = a->out;

@@ -209,6 +209,43 @@ __device__ __forceinline__ float wave_prefix_sum(float x)
     return x;
 }
 
+// In-kernel q/k normalisation of rows that lie in consecutive lanes, each lane
+// holding `n` bf16 elements of the row (8 lanes x 16 or 16 lanes x 8): the
+// sum of squares over the row's lanes, then x / sqrt(sum + eps), back to bf16.
+template <int LANES>
+__device__ __forceinline__ float row_lanes_sum(float x)
+{
+    static_assert(LANES == 8 || LANES == 16, "row width");
+    x += dpp_f<0xB1, 0xf>(x);    // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E, 0xf>(x);    // quad_perm [2,3,0,1]
+    x += dpp_f<0x141, 0xf>(x);   // row_half_mirror: the 8-lane half
+    if constexpr (LANES == 16) x += dpp_f<0x140, 0xf>(x);   // row_mirror: the other half
+    return x;
+}
+template <int LANES, int W>
+__device__ __forceinline__ void normalise_row(u32x4_t (&x)[W])
+{
+    float ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const uint32_t a[4] = {x[w].x, x[w].y, x[w].z, x[w].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ss = fmaf(bf16_lo(a[e]), bf16_lo(a[e]), ss);
+            ss = fmaf(bf16_hi(a[e]), bf16_hi(a[e]), ss);
+        }
+    }
+    const float r = qk_rnorm(row_lanes_sum<LANES>(ss));
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const uint32_t a[4] = {x[w].x, x[w].y, x[w].z, x[w].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(bf16_lo(a[e]) * r, bf16_hi(a[e]) * r);
+        x[w] = u32x4_t{o[0], o[1], o[2], o[3]};
+    }
+}
+
 // 16 consecutive elements (pieces a, b) into k-order: slots 0-3 and 12-15
 // stay, slots 4-7 take elements 8-11, slots 8-11 elements 4-7.
 __device__ __forceinline__ u32x4_t korder_lo(u32x4_t a, u32x4_t b) { return u32x4_t{a.x, a.y, b.x, b.y}; }
@@ -320,6 +357,15 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     u32x4_t kr[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) kr[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, t0 * DK * 2 + i * 1024 + lane * 16, 0, 0);
+    if (p.qk_norm) {
+        // Each load holds 4 whole rows, 16 lanes per row.
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            u32x4_t one[1] = {kr[i]};
+            normalise_row<16>(one);
+            kr[i] = one[0];
+        }
+    }
     bf16x8_t kf[2][8];
     unsigned char *kt = kst[wl];
 #pragma unroll
@@ -694,6 +740,14 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
+                    if (p.qk_norm) {
+                        // A row of K or Q spans 8 consecutive lanes, 32 bytes each.
+                        u32x4_t kx[2] = {ra[2 * m], ra[2 * m + 1]}, qx[2] = {ra[4 + 2 * m], ra[5 + 2 * m]};
+                        normalise_row<8>(kx);
+                        normalise_row<8>(qx);
+                        ra[2 * m] = kx[0]; ra[2 * m + 1] = kx[1];
+                        ra[4 + 2 * m] = qx[0]; ra[5 + 2 * m] = qx[1];
+                    }
                     *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
                     *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
                     *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp)) = korder_lo(ra[4 + 2 * m], ra[5 + 2 * m]);
@@ -897,6 +951,17 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkParams p)
             }
         }
         __syncthreads();
+        if (p.qk_norm) {
+            // k and q rows to x / sqrt(|x|^2 + eps); padded rows stay zero.
+            for (int r = tid; r < 2 * C; r += 256) {
+                float *row = (r < C ? Kc : Qc) + (r % C) * LD;
+                float ss = 0.f;
+                for (int d = 0; d < D; ++d) ss = fmaf(row[d], row[d], ss);
+                const float rn = qk_rnorm(ss);
+                for (int d = 0; d < D; ++d) row[d] *= rn;
+            }
+            __syncthreads();
+        }
         for (int e = tid; e < C * C; e += 256) {
             const int r = e / C, i = e % C;
             float kk = 0.f, qk = 0.f;

@@ -20,6 +20,7 @@ struct DecodeParams {
     float scale;
     int32_t B, Nk, Nv, S, slots;
     int32_t beta_logit;
+    int32_t qk_norm;     // q and k replaced by x / sqrt(sum(x^2) + 1e-6) in the kernel
 };
 
 // Kernel-side view of a chunked prefill call.
@@ -37,6 +38,7 @@ struct ChunkParams {
     float scale;
     int32_t B, Nk, Nv, S;
     int32_t beta_logit;
+    int32_t qk_norm;     // as in DecodeParams
 };
 
 // Bytes of workspace the chunk launcher needs for these sizes (0: none).
@@ -82,6 +84,10 @@ __device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias)
 {
     return -__expf(A_log) * gate_softplus(a + dt_bias);
 }
+// In-kernel q/k normalisation: 1 / sqrt(|x|^2 + 1e-6) (the blog post's l2norm;
+// deltanet.rs l2norm, eps inside the square root).
+constexpr float QK_NORM_EPS = 1e-6f;
+__device__ __forceinline__ float qk_rnorm(float sumsq) { return rsqrtf(sumsq + QK_NORM_EPS); }
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }

@@ -119,6 +119,22 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
         load_run<T, RPL>(k + qkoff, kr);
         load_run<T, RPL>(q + qkoff, qr);
         VecIO<T, VEC>::load(v + (vh * S + t) * DV + col, vv);
+        if (p.qk_norm) {
+            // q and k to x / sqrt(|x|^2 + eps): the rows of a column group sit
+            // in RG consecutive lanes.
+            float kk = 0.f, qq = 0.f;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                kk = fmaf(kr[i], kr[i], kk);
+                qq = fmaf(qr[i], qr[i], qq);
+            }
+            const float rk = qk_rnorm(group_sum<RG>(kk)), rq = qk_rnorm(group_sum<RG>(qq));
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                kr[i] *= rk;
+                qr[i] *= rq;
+            }
+        }
         const float braw = to_f32(beta[vh * S + t]);
         const float bt = p.beta_logit ? gate_sigmoid(braw) : braw;
 
@@ -285,13 +301,14 @@ __device__ __forceinline__ void s1_barrier()
 }
 
 // GK: per-key decay gk given. FG: fused gates, beta and g formed in the
-// kernel from the logits and the raw gate input a.
-template <bool GK, bool FG>
+// kernel from the logits and the raw gate input a. QN: q and k normalised in
+// the kernel.
+template <bool GK, bool FG, bool QN>
 __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, int nheads)
 {
     using namespace s1;
     __shared__ float4 red[2][NW][64];
-    __shared__ float redkq[2][NW];
+    __shared__ float4 redkq[2][NW];   // k . q, |k|^2, |q|^2 of each wave's rows
 
     const int lane = threadIdx.x & 63;
     const int j = uniform(threadIdx.x >> 6);
@@ -440,9 +457,26 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         t.z = rows_reduce4(sq[0], sq[2], sq[4], sq[6]);
         t.w = rows_reduce4(sq[1], sq[3], sq[5], sq[7]);
         kq = rows_sum(kq);
+        // |k|^2 and |q|^2 for the in-kernel normalisation.
+        float kk = 0.f, qq = 0.f;
+        if constexpr (QN) {
+            const float qr[NI] = {bf16_lo(H.q.x), bf16_hi(H.q.x), bf16_lo(H.q.y), bf16_hi(H.q.y)};
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                kk = fmaf(kr[i], kr[i], kk);
+                qq = fmaf(qr[i], qr[i], qq);
+            }
+            kk = rows_sum(kk);
+            qq = rows_sum(qq);
+        }
         // Over the workgroup.
         red[par][j][lane] = t;
-        if (lane == 0) redkq[par][j] = kq;
+        if (lane == 0) {
+            if constexpr (QN)
+                redkq[par][j] = float4{kq, kk, qq, 0.f};
+            else
+                redkq[par][j].x = kq;
+        }
         s1_barrier();
         float4 u = red[par][0][lane];
 #pragma unroll
@@ -450,11 +484,28 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
             const float4 x = red[par][w][lane];
             u.x += x.x; u.y += x.y; u.z += x.z; u.w += x.w;
         }
-        kq = 0.f;
+        float4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) kq += redkq[par][w];
+        for (int w = 0; w < NW; ++w) {
+            if constexpr (QN) {
+                const float4 x = redkq[par][w];
+                z.x += x.x; z.y += x.y; z.z += x.z;
+            } else {
+                z.x += redkq[par][w].x;
+            }
+        }
+        kq = z.x;
         par ^= 1;
         if constexpr (!GK) { u.x *= a; u.y *= a; u.z *= a; u.w *= a; }
+        // With normalised q and k, the sums scale by 1/|k| and 1/|q|, and the
+        // update takes k/|k|.
+        float rk = 1.f;
+        if constexpr (QN) {
+            rk = qk_rnorm(z.y);
+            const float rq = qk_rnorm(z.z);
+            u.x *= rk; u.y *= rk; u.z *= rq; u.w *= rq;
+            kq *= rk * rq;
+        }
         // delta of this lane row's two columns, then of all eight.
         const uint32_t vw = lr == 0 ? H.v.x : lr == 1 ? H.v.y : lr == 2 ? H.v.z : H.v.w;
         const float d0 = H.beta * (bf16_lo(vw) - u.x), d1 = H.beta * (bf16_hi(vw) - u.y);
@@ -464,7 +515,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         rows_gather(d0, e0);
         rows_gather(d1, e1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { dl[2 * r] = e0[r]; dl[2 * r + 1] = e1[r]; }
+        for (int r = 0; r < 4; ++r) { dl[2 * r] = e0[r] * rk; dl[2 * r + 1] = e1[r] * rk; }
         // S' = D S + k delta^T, stored at once.
         const auto srs = brsrc(pool + ((size_t)H.r * Nv + H.h) * DK * DV, DK * DV * 2);
 #pragma unroll
@@ -543,12 +594,12 @@ struct MTTok {
     int w;               // the token's write slot
 };
 
-template <bool GK, bool FG>
-__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))) void decode_mt_kernel(DecodeParams p)
+template <bool GK, bool FG, bool QN>
+__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(GK && (FG || QN) ? 3 : 4))) void decode_mt_kernel(DecodeParams p)
 {
     using namespace mt;
     __shared__ float4 red[2][NW][64];
-    __shared__ float redkq[2][NW];
+    __shared__ float4 redkq[2][NW];   // k . q, |k|^2, |q|^2 of each wave's rows
 
     const int lane = threadIdx.x & 63;
     const int j = uniform(threadIdx.x >> 6);
@@ -659,11 +710,26 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
         tt.z = rows_reduce4(sq[0], sq[2], sq[4], sq[6]);
         tt.w = rows_reduce4(sq[1], sq[3], sq[5], sq[7]);
         kq = rows_sum(kq);
+        float kk = 0.f, qq = 0.f;   // |k|^2, |q|^2 for the in-kernel normalisation
+        if constexpr (QN) {
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                kk = fmaf(kr[i], kr[i], kk);
+                qq = fmaf(qr[i], qr[i], qq);
+            }
+            kk = rows_sum(kk);
+            qq = rows_sum(qq);
+        }
         // Over the workgroup. The two buffers alternate by token: a wave can
         // write the next token's sums only after every wave has passed this
         // token's barrier, so after every read of the other buffer.
         red[par][j][lane] = tt;
-        if (lane == 0) redkq[par][j] = kq;
+        if (lane == 0) {
+            if constexpr (QN)
+                redkq[par][j] = float4{kq, kk, qq, 0.f};
+            else
+                redkq[par][j].x = kq;
+        }
         s1_barrier();
         float4 u = red[par][0][lane];
 #pragma unroll
@@ -671,10 +737,27 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
             const float4 x = red[par][w][lane];
             u.x += x.x; u.y += x.y; u.z += x.z; u.w += x.w;
         }
-        kq = redkq[par][0];
+        float4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 1; w < NW; ++w) kq += redkq[par][w];
+        for (int w = 0; w < NW; ++w) {
+            if constexpr (QN) {
+                const float4 x = redkq[par][w];
+                z.x += x.x; z.y += x.y; z.z += x.z;
+            } else {
+                z.x += redkq[par][w].x;
+            }
+        }
+        kq = z.x;
         par ^= 1;
+        // With normalised q and k the sums scale by 1/|k| and 1/|q|, and the
+        // update takes k/|k|.
+        float rk = 1.f;
+        if constexpr (QN) {
+            rk = qk_rnorm(z.y);
+            const float rq = qk_rnorm(z.z);
+            u.x *= rk; u.y *= rk; u.z *= rq; u.w *= rq;
+            kq *= rk * rq;
+        }
         const float beta = FG ? gate_sigmoid(__uint_as_float(cur.beta << 16)) : __uint_as_float(cur.beta << 16);
         const uint32_t vw = lr == 0 ? cur.v.x : lr == 1 ? cur.v.y : lr == 2 ? cur.v.z : cur.v.w;
         const float d0 = beta * (bf16_lo(vw) - u.x), d1 = beta * (bf16_hi(vw) - u.y);
@@ -683,7 +766,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(4))
         rows_gather(d0, e0);
         rows_gather(d1, e1);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) { dl[2 * q4] = e0[q4]; dl[2 * q4 + 1] = e1[q4]; }
+        for (int q4 = 0; q4 < 4; ++q4) { dl[2 * q4] = e0[q4] * rk; dl[2 * q4 + 1] = e1[q4] * rk; }
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -755,16 +838,24 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
         DecodeParams pc = p;
         int nh = nheads;
         void *args[] = {&pc, &nh};
-        const void *fn = p.gate_a ? (p.gk ? (const void *)decode_s1_kernel<true, true> : (const void *)decode_s1_kernel<false, true>)
-                                  : (p.gk ? (const void *)decode_s1_kernel<true, false> : (const void *)decode_s1_kernel<false, false>);
+        static const void *const fns[8] = {
+            (const void *)decode_s1_kernel<false, false, false>, (const void *)decode_s1_kernel<true, false, false>,
+            (const void *)decode_s1_kernel<false, true, false>,  (const void *)decode_s1_kernel<true, true, false>,
+            (const void *)decode_s1_kernel<false, false, true>,  (const void *)decode_s1_kernel<true, false, true>,
+            (const void *)decode_s1_kernel<false, true, true>,   (const void *)decode_s1_kernel<true, true, true>};
+        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0)];
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
     if (dtype == 1 && p.S >= 2 && Dk == mt::DK && Dv == mt::DV) {
         *supported = true;
         DecodeParams pc = p;
         void *args[] = {&pc};
-        const void *fn = p.gate_a ? (p.gk ? (const void *)decode_mt_kernel<true, true> : (const void *)decode_mt_kernel<false, true>)
-                                  : (p.gk ? (const void *)decode_mt_kernel<true, false> : (const void *)decode_mt_kernel<false, false>);
+        static const void *const fns[8] = {
+            (const void *)decode_mt_kernel<false, false, false>, (const void *)decode_mt_kernel<true, false, false>,
+            (const void *)decode_mt_kernel<false, true, false>,  (const void *)decode_mt_kernel<true, true, false>,
+            (const void *)decode_mt_kernel<false, false, true>,  (const void *)decode_mt_kernel<true, false, true>,
+            (const void *)decode_mt_kernel<false, true, true>,   (const void *)decode_mt_kernel<true, true, true>};
+        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0)];
         return hipLaunchKernel(fn, dim3((unsigned)(p.B * p.Nv)), dim3(64 * mt::NW), args, 0, s);
     }
     if (dtype == 1) return launch_typed<bf16_t>(Dk, Dv, p, s, supported);

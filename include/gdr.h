@@ -35,6 +35,11 @@
  *    (Nv) float32 per value head. The four come together, in place of beta
  *    and g (which must then be NULL). The gates are formed in float32 and
  *    never stored; positions t >= L_b are never read.
+ *  - In-kernel q/k normalisation (optional, both calls): with use_qk_l2norm
+ *    nonzero, q and k are replaced by x / sqrt(sum(x^2) + 1e-6) over the head
+ *    dimension before use (the blog post's use_qk_l2norm_in_kernel; deltanet.rs
+ *    l2norm, with eps inside the square root). Otherwise callers pass
+ *    normalised vectors.
  *  - Return codes are produced on the host before anything is enqueued
  *    (except GDR_ERR_LAUNCH, from the launch itself). No value of g or gk is
  *    checked (the operator pages leave their sign unchecked on purpose).
@@ -77,7 +82,8 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  * Sizes: B >= 0 sequences, 1 <= S <= 8 token positions per sequence,
  *        Nk, Nv heads, head sizes Dk, Dv, num_slots >= 1 pool slots.
  * Tensors (device, row-major):
- *   q, k      (B, Nk, S, Dk)   dtype; callers pass L2-normalised vectors
+ *   q, k      (B, Nk, S, Dk)   dtype; L2-normalised by the caller unless
+ *                              use_qk_l2norm is set
  *   v         (B, Nv, S, Dv)   dtype
  *   beta      (B, Nv, S)       dtype, write strength in [0, 1] (NULL with
  *                              fused gates)
@@ -128,6 +134,7 @@ typedef struct {
     const void *beta_logits;
     const void *gate_a;
     const float *A_log, *dt_bias;
+    int32_t use_qk_l2norm;   /* 0: q and k used as given */
 } gdr_decode_args;
 
 GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
@@ -193,6 +200,7 @@ typedef struct {
     const void *beta_logits;
     const void *gate_a;
     const float *A_log, *dt_bias;
+    int32_t use_qk_l2norm;   /* 0: q and k used as given */
 } gdr_chunk_args;
 
 GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);

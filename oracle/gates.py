@@ -1,4 +1,5 @@
-"""Fused gates of the Gated DeltaNet layer, in float64 — TEST INFRASTRUCTURE ONLY.
+"""Fused preprocessing of the Gated DeltaNet layer, in float64 — TEST
+INFRASTRUCTURE ONLY: the gates, and the optional q/k normalisation.
 
 The Gated DeltaNet blog post's layer code forms the write strength and the log
 decay right before the recurrence, from the gate projections b and a and the
@@ -11,6 +12,10 @@ them per token in its recurrent step, its chunk form and its step/chunk
 kernels. Written out here from those definitions, with
 sigmoid(x) = 1 / (1 + e^-x) and softplus(x) = ln(1 + e^x). The recurrence
 oracle then takes beta and g as usual.
+
+With use_qk_l2norm_in_kernel the blog post's recurrent and chunk functions
+first replace q and k by l2norm(x) = x / sqrt(sum(x^2) + 1e-6) over the head
+dimension; deltanet.rs's l2norm is the same, eps inside the square root.
 """
 import numpy as np
 
@@ -44,3 +49,9 @@ def gates(beta_logits, a, A_log, dt_bias):
     A_log = np.asarray(A_log, dtype=np.float64)[:, None]
     dt_bias = np.asarray(dt_bias, dtype=np.float64)[:, None]
     return sigmoid(b), -np.exp(A_log) * softplus(a + dt_bias)
+
+
+def l2norm(x, eps=1e-6):
+    """x / sqrt(sum(x^2) + eps) over the last axis, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt((x * x).sum(-1, keepdims=True) + eps)

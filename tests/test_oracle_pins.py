@@ -332,3 +332,18 @@ def test_gate_closed_forms():
     assert np.all(g < 0)
     order = np.argsort(a[0, 1])
     assert np.all(np.diff(g[0, 1][order]) <= 0)
+
+
+def test_l2norm_closed_forms():
+    from oracle.gates import l2norm
+    e = 1e-6
+    x = np.zeros((2, 5))
+    x[0, 2] = 3.0
+    y = l2norm(x)
+    assert y[0, 2] == 3.0 / math.sqrt(9.0 + e) and np.all(np.delete(y[0], 2) == 0)
+    assert np.all(y[1] == 0)                                                  # zero vector stays zero
+    r = np.random.default_rng(8).standard_normal((64, 128)) * 5
+    n = np.sqrt((r * r).sum(-1))
+    ny = np.sqrt((l2norm(r) ** 2).sum(-1))
+    assert np.abs(ny - n / np.sqrt(n * n + e)).max() < 1e-15                   # norm closed form
+    assert np.abs(l2norm(r) * np.sqrt(n * n + e)[:, None] - r).max() < 1e-12  # direction kept
