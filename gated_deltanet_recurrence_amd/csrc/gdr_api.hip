@@ -7,6 +7,7 @@
 namespace {
 
 bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 // Either beta (and optionally g), or the fused gates: the logits, a, A_log and
 // dt_bias together, with neither beta nor g.
@@ -60,7 +61,8 @@ gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
     if (gs != GDR_OK) return gs;
     if ((int64_t)a->B * a->Nv * 2 > 0x7fffffffLL) return GDR_ERR_UNSUPPORTED;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->state_pool) ||
-        !aligned16(a->out) || !aligned16(a->gk))
+        !aligned16(a->out) || !aligned16(a->gk) || !aligned4(a->beta) || !aligned4(a->beta_logits) ||
+        !aligned4(a->gate_a) || !aligned4(a->g) || !aligned4(a->A_log) || !aligned4(a->dt_bias))
         return GDR_ERR_UNSUPPORTED;
 
     gdr::DecodeParams p;
@@ -99,7 +101,9 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     const gdr_status gs = check_gates(a->beta, a->beta_logits, a->g, a->gate_a, a->A_log, a->dt_bias);
     if (gs != GDR_OK) return gs;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) ||
-        !aligned16(a->initial_state) || !aligned16(a->final_state) || !aligned16(a->workspace))
+        !aligned16(a->initial_state) || !aligned16(a->final_state) || !aligned16(a->workspace) ||
+        !aligned4(a->beta) || !aligned4(a->beta_logits) || !aligned4(a->gate_a) || !aligned4(a->g) ||
+        !aligned4(a->A_log) || !aligned4(a->dt_bias))
         return GDR_ERR_UNSUPPORTED;
     // 32-bit offsets inside the kernels: one head plane and the chunk count.
     if ((int64_t)a->S * a->Dk * 4 > 0x7fffffffLL || (int64_t)a->S * a->Dv * 4 > 0x7fffffffLL ||

@@ -44,7 +44,8 @@
  *    (except GDR_ERR_LAUNCH, from the launch itself). No value of g or gk is
  *    checked (the operator pages leave their sign unchecked on purpose).
  *  - Inputs and outputs must not overlap, except where stated.
- *  - q, k, v, the states, out and gk must be 16-byte aligned
+ *  - q, k, v, the states, out and gk must be 16-byte aligned, and beta, g,
+ *    beta_logits, gate_a, A_log and dt_bias 4-byte aligned
  *    (GDR_ERR_UNSUPPORTED otherwise); torch allocations always are.
  */
 #ifndef GDR_H

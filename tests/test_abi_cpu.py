@@ -93,6 +93,9 @@ _GATE_CASES = [
     (dict(_FUSED, dt_bias=None), gdr.GDR_ERR_NULL),
     (dict(beta_logits=FAKE), gdr.GDR_ERR_SHAPE),
     (dict(_FUSED, Dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(_FUSED, gate_a=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(_FUSED, beta_logits=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(beta=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
     (dict(_FUSED, B=0, num_state_indices=0, q=None, out=None, workspace=None), gdr.GDR_OK),
 ]
 
