@@ -127,6 +127,15 @@ def test_decay_extremes(gate):
     _check_full(c, out, fin)
 
 
+@pytest.mark.parametrize("Nk,Nv", [(3, 3), (1, 8)])
+def test_head_grouping(Nk, Nv):
+    # one value head per key head, and eight: the workgroup groups that share
+    # q/k (and are kept on one XCD) are 2 and 16 units wide
+    c = synth.config(4, B=5, Nk=Nk, Nv=Nv, S=200, lens=[200, 64, 1, 0, 133], base=440 + Nv)
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
 def test_resume_equals_one_shot():
     # prefill of 200 tokens, then 170 more from the returned state, against the
     # oracle's single 370-token pass (the intermediate state is stored in bf16)
