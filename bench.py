@@ -247,8 +247,19 @@ def cpu_baseline_decode(c, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": tokens * reps / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"the whole decode step workload ({c.B} sequences x {c.Nv} heads), {reps} calls, {el:.1f} s"}
+    res = {"value": tokens * reps / el, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"the whole decode step workload ({c.B} sequences x {c.Nv} heads), {reps} calls, {el:.1f} s"}
+    # the same on one thread
+    reps1, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(*args, nthreads=1)
+        reps1 += 1
+        el1 = time.perf_counter() - t0
+        if el1 >= budget_s / 4:
+            break
+    res["single_thread"] = {"value": tokens * reps1 / el1, "unit": "tok/s", "cores": 1,
+                            "sample": f"{reps1} calls, {el1:.1f} s"}
+    return res
 
 
 def cpu_baseline_prefill(c, units, name):
