@@ -133,9 +133,16 @@ def prefill_work(c, fused=False):
 # ---------------------------------------------------------------------------
 # timing
 # ---------------------------------------------------------------------------
+WARM_S = 0.3   # untimed warm-up of at least this long before every timed run
+
+
 def time_calls(calls, steps, warmup, use_graph):
     """Runs `warmup` then `steps` calls (cycling through `calls`), timed with
-    HIP events on the current stream. Returns (ms per call by events, wall s)."""
+    HIP events on the current stream. Returns (ms per call by events, wall s).
+    The warm-up continues, untimed, until it has lasted WARM_S seconds: the
+    GPU's clock ramps up over a few milliseconds of sustained work, and a
+    short call run after an idle phase would otherwise be timed partly at
+    idle clock."""
     stream = torch.cuda.current_stream()
     n = len(calls)
     if use_graph:
@@ -147,9 +154,14 @@ def time_calls(calls, steps, warmup, use_graph):
             for i in range(n):
                 calls[i]()
         reps_w = max(1, math.ceil(warmup / n))
+        t_w = time.perf_counter()
         for _ in range(reps_w):
             graph.replay()
         torch.cuda.synchronize()
+        while time.perf_counter() - t_w < WARM_S:
+            for _ in range(reps_w):
+                graph.replay()
+            torch.cuda.synchronize()
         reps = max(1, math.ceil(steps / n))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
@@ -160,8 +172,13 @@ def time_calls(calls, steps, warmup, use_graph):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / (reps * n), wall, reps * n
-    for i in range(warmup):
+    t_w = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_w < WARM_S:
         calls[i % n]()
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
