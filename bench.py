@@ -89,9 +89,10 @@ def gate_bytes(c, fused):
     return 2 * e if fused else e + (4 if c.g is not None else 0)
 
 
-def decode_bytes(c, fused=False):
+def decode_bytes(c, fused=False, norm=False):
     """State read once per active sequence and written once per distinct
-    consecutive write slot, plus token inputs, outputs and integers."""
+    consecutive write slot, plus token inputs, outputs and integers (and with
+    the gated RMSNorm epilogue its z of every valid token and its w)."""
     e = esize(c.dtype)
     L = c.valid_lengths()
     S, slots = c.S, c.state.shape[0]
@@ -110,20 +111,22 @@ def decode_bytes(c, fused=False):
         state += hs * (1 + writes)
         tok += int(L[b])
     per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * gate_bytes(c, fused) \
-        + (4 * c.Nv * c.Dk if c.gk is not None else 0)
-    out = c.B * c.S * c.Nv * c.Dv * e
+        + (4 * c.Nv * c.Dk if c.gk is not None else 0) + (c.Nv * c.Dv * e if norm else 0)
+    out = c.B * c.S * c.Nv * c.Dv * e + (4 * c.Dv if norm else 0)
     ints = c.B * 4 * (2 if c.n_acc is not None else 1) + c.B * c.S * 4 + (8 * c.Nv if fused else 0)
     return state, state + tok * per_tok + out + ints, tok
 
 
-def prefill_work(c, fused=False):
+def prefill_work(c, fused=False, norm=False):
     """(bytes, flops) per call. Flops per token and value head:
-    C(3Dk + 2Dv) + C^2/3 + 6 Dk Dv (triangular products counted at half)."""
+    C(3Dk + 2Dv) + C^2/3 + 6 Dk Dv (triangular products counted at half).
+    The gated RMSNorm epilogue adds its z (and w) to the bytes; its flops are
+    left out."""
     e = esize(c.dtype)
     L = c.valid_lengths()
     T = int(L.sum())
-    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * gate_bytes(c, fused)
-    out = c.B * c.S * c.Nv * c.Dv * e + (8 * c.Nv if fused else 0)
+    per_tok = 2 * c.Nk * c.Dk * e + c.Nv * c.Dv * e + c.Nv * gate_bytes(c, fused) + (c.Nv * c.Dv * e if norm else 0)
+    out = c.B * c.S * c.Nv * c.Dv * e + (8 * c.Nv if fused else 0) + (4 * c.Dv if norm else 0)
     states = c.B * c.Nv * c.Dk * c.Dv * e * ((1 if c.state is not None else 0) + 1)
     C = c.chunk
     f_tok = C * (3 * c.Dk + 2 * c.Dv) + C * C / 3 + 6 * c.Dk * c.Dv
@@ -197,9 +200,19 @@ def fused_gate_tensors(c, fused):
     return None if fused is None else [dev(x) for x in fused]
 
 
-def decode_calls(c, copies, fused=None):
+def norm_fields(a, t, c, norm):
+    """Puts the gated RMSNorm epilogue's (z, w) storage arrays (synth.norm_inputs)
+    on the device and into the marshalled arguments a (eps 1e-6)."""
+    if norm is None:
+        return
+    t["nz"], t["nw"] = dev(norm[0]), dev(norm[1])
+    a.norm_z, a.norm_w, a.norm_eps = t["nz"].data_ptr(), t["nw"].data_ptr(), 1e-6
+
+
+def decode_calls(c, copies, fused=None, norm=None):
     """Pre-marshalled gdr_decode calls, one per copy of the pool and inputs.
-    fused: None, or the fused-gate storage arrays (synth.gate_inputs)."""
+    fused: None, or the fused-gate storage arrays (synth.gate_inputs); norm:
+    None, or the epilogue's (synth.norm_inputs)."""
     lib = gdr.load_library()
     calls, keep = [], []
     for _ in range(copies):
@@ -213,6 +226,7 @@ def decode_calls(c, copies, fused=None):
                            c.Dk, c.Dv, c.state.shape[0], c.idx.size, p(t["q"]), p(t["k"]), p(t["v"]),
                            p(t["beta"]), p(t["g"]), p(t["gk"]), p(t["pool"]), p(t["lens"]), p(t["idx"]),
                            p(t["nacc"]), c.scale, p(t["out"]), *[p(x) for x in (t["gates"] or [None] * 4)])
+        norm_fields(a, t, c, norm)
         keep.append((t, a))
 
         def call(a=a):
@@ -223,7 +237,7 @@ def decode_calls(c, copies, fused=None):
     return calls, keep
 
 
-def chunk_calls(c, copies, fused=None):
+def chunk_calls(c, copies, fused=None, norm=None):
     lib = gdr.load_library()
     calls, keep = [], []
     for _ in range(copies):
@@ -237,6 +251,7 @@ def chunk_calls(c, copies, fused=None):
                           c.Dv, c.chunk, p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["g"]),
                           p(t["init"]), p(t["lens"]), c.scale, p(t["out"]), p(t["fin"]), None, 0,
                           *[p(x) for x in (t["gates"] or [None] * 4)])
+        norm_fields(a, t, c, norm)
         t["ws"] = gdr.chunk_workspace(a, torch.device("cuda"))
         keep.append((t, a))
 
@@ -312,7 +327,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="decode pool copies rotated per step")
     ap.add_argument("--varlen", action="store_true", help="also time the varlen prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused"], default=None)
+    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused", "norm"], default=None)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -413,6 +428,43 @@ def main():
                           "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
                           "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel (fused gates)", "bound": "mfma",
+                                       "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                                       "algorithmic_flops_per_launch": flops,
+                                       "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls, c
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "norm"):
+        # The decode step and chunked prefill workloads with the gated RMSNorm
+        # output epilogue (z in bf16, w float32): in the decode kernel itself,
+        # and as a pass of its own after the prefill kernels.
+        log("decode step workload, gated RMSNorm epilogue")
+        c = synth.config(2)
+        state_b, bytes_call, tok = decode_bytes(c, norm=True)
+        calls, keep = decode_calls(c, args.copies, norm=synth.norm_inputs(202, c.B, c.Nv, c.S, c.Dv, c.dtype))
+        ms, wall, _ = time_calls(calls, args.steps, args.warmup, use_graph)
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        secondary.append({"workload": "decode step, gated RMSNorm epilogue: B=64 Nk=16 Nv=32 S=1 Dk=Dv=128 bf16, "
+                                      "z in bf16, w float32",
+                          "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "state_GBps": state_b / (ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "decode_s1_kernel (epilogue in the kernel)", "bound": "hbm",
+                                       "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                       "traffic": None, "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls
+        torch.cuda.empty_cache()
+        log("chunked prefill workload, gated RMSNorm epilogue")
+        c = synth.config(4)
+        bytes_call, flops, tok = prefill_work(c, norm=True)
+        calls, keep = chunk_calls(c, 2, norm=synth.norm_inputs(404, c.B, c.Nv, c.S, c.Dv, c.dtype))
+        ms, wall, _ = time_calls(calls, max(10, args.steps // 8), max(2, args.warmup // 8), use_graph)
+        tf = flops / (ms * 1e-3) / 1e12
+        secondary.append({"workload": "chunked prefill, gated RMSNorm epilogue: B=4 S=4096 Nk=16 Nv=32 Dk=Dv=128 "
+                                      "bf16, g, initial state, C=64, z in bf16, w float32",
+                          "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel + norm_kernel", "bound": "mfma",
                                        "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                        "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
                                        "algorithmic_flops_per_launch": flops,

@@ -39,6 +39,7 @@ class DecodeArgs(ctypes.Structure):
         ("scale_value", ctypes.c_float), ("out", _vp),
         ("beta_logits", _vp), ("gate_a", _vp), ("A_log", _vp), ("dt_bias", _vp),
         ("use_qk_l2norm", ctypes.c_int32),
+        ("norm_z", _vp), ("norm_w", _vp), ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -53,6 +54,7 @@ class ChunkArgs(ctypes.Structure):
         ("workspace", _vp), ("workspace_bytes", ctypes.c_int64),
         ("beta_logits", _vp), ("gate_a", _vp), ("A_log", _vp), ("dt_bias", _vp),
         ("use_qk_l2norm", ctypes.c_int32),
+        ("norm_z", _vp), ("norm_w", _vp), ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -140,8 +142,25 @@ def _gates(beta, g, gates, dt, dev, B, Nv, S):
     return _ptr(bl), _ptr(ga), _ptr(al), _ptr(db)
 
 
+def _norm(norm, dt, dev, B, Nv, S, Dv):
+    """Checks the gated RMSNorm epilogue's (z, w, eps) and returns its ABI
+    fields (None, None, 0.0 when unused)."""
+    if norm is None:
+        return None, None, 0.0
+    try:
+        z, w, eps = norm
+    except (TypeError, ValueError):
+        raise ValueError("norm must be (z, w, eps)")
+    if z is None or w is None:
+        raise ValueError("the epilogue needs both z and w")
+    _need(z, "norm z", dt, dev, (B, Nv, S, Dv))
+    _need(w, "norm w", torch.float32, dev, (Dv,))
+    return _ptr(z), _ptr(w), float(eps)
+
+
 def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices, g=None, gk=None,
-               num_accepted_tokens=None, scale_value=1.0, out=None, gates=None, use_qk_l2norm=False):
+               num_accepted_tokens=None, scale_value=1.0, out=None, gates=None, use_qk_l2norm=False,
+               norm=None):
     """Recurrent decode; updates state_pool in place. Returns (out, state_pool).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); state_pool
@@ -152,7 +171,10 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     in the dtype, A_log and dt_bias (Nv,) float32 — in place of beta and g
     (pass beta=None): the kernels form beta = sigmoid(beta_logits) and
     g = -exp(A_log) * softplus(a + dt_bias). use_qk_l2norm: the kernels
-    normalise q and k (x / sqrt(sum(x^2) + 1e-6)) before use.
+    normalise q and k (x / sqrt(sum(x^2) + 1e-6)) before use. norm: None, or
+    (z, w, eps) — z (B, Nv, S, Dv) in the dtype, w (Dv,) float32 — for the
+    gated RMSNorm epilogue o * w * silu(z) / sqrt(mean(o^2) + eps) on every
+    valid output row.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
@@ -181,19 +203,20 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     a = DecodeArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, state_pool.shape[0], ssm_state_indices.numel(),
                    _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(gk), _ptr(state_pool),
                    _ptr(actual_seq_lengths), _ptr(ssm_state_indices), _ptr(num_accepted_tokens),
-                   float(scale_value), _ptr(out), *fused, int(bool(use_qk_l2norm)))
+                   float(scale_value), _ptr(out), *fused, int(bool(use_qk_l2norm)),
+                   *_norm(norm, dt, dev, B, Nv, S, Dv))
     _check(load_library().gdr_decode(ctypes.byref(a), _stream(dev)), "gdr_decode")
     return out, state_pool
 
 
 def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
-              chunk_size=64, out=None, final_state=None, gates=None, use_qk_l2norm=False):
+              chunk_size=64, out=None, final_state=None, gates=None, use_qk_l2norm=False, norm=None):
     """Chunked prefill. Returns (out, final_state).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); initial_state
     (B, Nv, Dk, Dv) or None — one dtype; g (B, Nv, S) float32 or None;
     actual_seq_lengths (B,) int32 or None. final_state may be initial_state
-    itself (updated in place). gates, use_qk_l2norm: as for gdr_decode.
+    itself (updated in place). gates, use_qk_l2norm, norm: as for gdr_decode.
     """
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
@@ -220,7 +243,7 @@ def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None
     a = ChunkArgs(_DT[dt], B, Nk, Nv, S, Dk, Dv, int(chunk_size),
                   _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
                   _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state),
-                  None, 0, *fused, int(bool(use_qk_l2norm)))
+                  None, 0, *fused, int(bool(use_qk_l2norm)), *_norm(norm, dt, dev, B, Nv, S, Dv))
     lib = load_library()
     ws = chunk_workspace(a, dev)
     _check(lib.gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")

@@ -20,10 +20,30 @@ gdr_status check_gates(const void *beta, const void *logits, const float *g, con
     return GDR_OK;
 }
 
+// The epilogue's z and w come together; eps must be a number >= 0.
+gdr_status check_norm(const void *z, const float *w, float eps)
+{
+    if (!z && !w) return GDR_OK;
+    if (!z || !w) return GDR_ERR_NULL;
+    if (!(eps >= 0.f)) return GDR_ERR_SHAPE;
+    return GDR_OK;
+}
+
 gdr_status from_launch(hipError_t e, bool supported)
 {
     if (!supported) return GDR_ERR_UNSUPPORTED;
     return e == hipSuccess ? GDR_OK : GDR_ERR_LAUNCH;
+}
+
+// The epilogue as a separate pass over out, after the call's main kernels
+// (same stream).
+template <typename Args>
+hipError_t launch_norm_pass(const Args *a, void *stream, bool *ok)
+{
+    gdr::NormParams n;
+    n.out = a->out; n.z = a->norm_z; n.w = a->norm_w; n.lens = a->actual_seq_lengths; n.eps = a->norm_eps;
+    n.B = a->B; n.Nv = a->Nv; n.S = a->S; n.Dv = a->Dv;
+    return gdr::launch_norm(a->dtype, n, (hipStream_t)stream, ok);
 }
 
 }  // namespace
@@ -59,9 +79,13 @@ gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
         return GDR_ERR_NULL;
     const gdr_status gs = check_gates(a->beta, a->beta_logits, a->g, a->gate_a, a->A_log, a->dt_bias);
     if (gs != GDR_OK) return gs;
+    const gdr_status ns = check_norm(a->norm_z, a->norm_w, a->norm_eps);
+    if (ns != GDR_OK) return ns;
     if ((int64_t)a->B * a->Nv * 2 > 0x7fffffffLL) return GDR_ERR_UNSUPPORTED;
+    if (a->norm_z && !gdr::norm_supported(a->Dv, a->B, a->Nv, a->S)) return GDR_ERR_UNSUPPORTED;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->state_pool) ||
-        !aligned16(a->out) || !aligned16(a->gk) || !aligned4(a->beta) || !aligned4(a->beta_logits) ||
+        !aligned16(a->out) || !aligned16(a->gk) || !aligned16(a->norm_z) || !aligned16(a->norm_w) ||
+        !aligned4(a->beta) || !aligned4(a->beta_logits) ||
         !aligned4(a->gate_a) || !aligned4(a->g) || !aligned4(a->A_log) || !aligned4(a->dt_bias))
         return GDR_ERR_UNSUPPORTED;
 
@@ -77,8 +101,10 @@ gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
     p.out = a->out;
     p.scale = a->scale_value;
     p.B = a->B; p.Nk = a->Nk; p.Nv = a->Nv; p.S = a->S; p.slots = a->num_slots;
-    bool ok = false;
-    hipError_t e = gdr::launch_decode(a->dtype, a->Dk, a->Dv, p, (hipStream_t)stream, &ok);
+    p.norm_z = a->norm_z; p.norm_w = a->norm_w; p.norm_eps = a->norm_eps;
+    bool ok = false, norm_done = false;
+    hipError_t e = gdr::launch_decode(a->dtype, a->Dk, a->Dv, p, (hipStream_t)stream, &ok, &norm_done);
+    if (e == hipSuccess && ok && a->norm_z && !norm_done) e = launch_norm_pass(a, stream, &ok);
     return from_launch(e, ok);
 }
 
@@ -100,8 +126,11 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     if (!a->q || !a->k || !a->v || !a->out || !a->final_state) return GDR_ERR_NULL;
     const gdr_status gs = check_gates(a->beta, a->beta_logits, a->g, a->gate_a, a->A_log, a->dt_bias);
     if (gs != GDR_OK) return gs;
+    const gdr_status ns = check_norm(a->norm_z, a->norm_w, a->norm_eps);
+    if (ns != GDR_OK) return ns;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) ||
         !aligned16(a->initial_state) || !aligned16(a->final_state) || !aligned16(a->workspace) ||
+        !aligned16(a->norm_z) || !aligned16(a->norm_w) ||
         !aligned4(a->beta) || !aligned4(a->beta_logits) || !aligned4(a->gate_a) || !aligned4(a->g) ||
         !aligned4(a->A_log) || !aligned4(a->dt_bias))
         return GDR_ERR_UNSUPPORTED;
@@ -109,6 +138,7 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     if ((int64_t)a->S * a->Dk * 4 > 0x7fffffffLL || (int64_t)a->S * a->Dv * 4 > 0x7fffffffLL ||
         (int64_t)a->B * a->Nv * (a->S / a->chunk_size + 1) > 0x7ffffff0LL)
         return GDR_ERR_UNSUPPORTED;
+    if (a->norm_z && !gdr::norm_supported(a->Dv, a->B, a->Nv, a->S)) return GDR_ERR_UNSUPPORTED;
     const int64_t need = gdr_chunk_workspace_size(a);
     if (need > 0 && !a->workspace) return GDR_ERR_NULL;
     if (need > a->workspace_bytes) return GDR_ERR_SHAPE;
@@ -129,6 +159,7 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     p.B = a->B; p.Nk = a->Nk; p.Nv = a->Nv; p.S = a->S;
     bool ok = false;
     hipError_t e = gdr::launch_chunk(a->dtype, a->Dk, a->Dv, a->chunk_size, p, (hipStream_t)stream, &ok);
+    if (e == hipSuccess && ok && a->norm_z) e = launch_norm_pass(a, stream, &ok);
     return from_launch(e, ok);
 }
 

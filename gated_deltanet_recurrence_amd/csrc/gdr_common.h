@@ -21,6 +21,10 @@ struct DecodeParams {
     int32_t B, Nk, Nv, S, slots;
     int32_t beta_logit;
     int32_t qk_norm;     // q and k replaced by x / sqrt(sum(x^2) + 1e-6) in the kernel
+    // Gated RMSNorm epilogue (norm_z NULL: none): z in dtype, w float32.
+    const void *norm_z;
+    const float *norm_w;
+    float norm_eps;
 };
 
 // Kernel-side view of a chunked prefill call.
@@ -41,12 +45,29 @@ struct ChunkParams {
     int32_t qk_norm;     // as in DecodeParams
 };
 
+// The gated RMSNorm epilogue as a pass of its own over the rows of out
+// (B, Nv, S, Dv): rows t < clamp(lens[b], 0, S) (all S when lens is NULL) are
+// replaced in place; the others are left alone.
+struct NormParams {
+    void *out;
+    const void *z;
+    const float *w;
+    const int32_t *lens;
+    float eps;
+    int32_t B, Nv, S, Dv;
+};
+
 // Bytes of workspace the chunk launcher needs for these sizes (0: none).
 int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, int S);
 
 // Launchers: return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
-hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported);
+// launch_decode sets *norm_done when the chosen kernel applied the epilogue itself.
+hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported,
+                         bool *norm_done);
 hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, hipStream_t s, bool *supported);
+hipError_t launch_norm(int dtype, const NormParams &p, hipStream_t s, bool *supported);
+// Whether launch_norm can take these sizes (checked before a call enqueues anything).
+bool norm_supported(int Dv, int B, int Nv, int S);
 
 // ---------------------------------------------------------------------------
 // Element access helpers (device). bf16 values travel as raw 16-bit patterns;
@@ -88,6 +109,16 @@ __device__ __forceinline__ float gate_g(float a, float A_log, float dt_bias)
 // deltanet.rs l2norm, eps inside the square root).
 constexpr float QK_NORM_EPS = 1e-6f;
 __device__ __forceinline__ float qk_rnorm(float sumsq) { return rsqrtf(sumsq + QK_NORM_EPS); }
+
+// Gated RMSNorm epilogue (inferencelayer deltanet.rs, the per-head gated
+// RMSNorm): o_j w_j silu(z_j) / sqrt(mean(o^2) + eps), silu(x) = x / (1 + e^-x).
+// An all-zero row stays zero: its factor is taken as 0 when mean + eps is 0.
+__device__ __forceinline__ float norm_silu(float z) { return z / (1.f + __expf(-z)); }
+__device__ __forceinline__ float norm_rinv(float sumsq, int Dv, float eps)
+{
+    const float m = sumsq / (float)Dv + eps;
+    return m > 0.f ? 1.f / sqrtf(m) : 0.f;
+}
 
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }

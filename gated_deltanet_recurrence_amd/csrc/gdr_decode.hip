@@ -254,12 +254,24 @@ struct S1Head {
     u32x2_t k, q;         // the lane's 4 rows of k and q (bf16)
     u32x4_t v;            // the lane's 8 columns of v (bf16)
     u32x4_t gk;           // the lane's 4 rows of gk (f32)
+    uint32_t z;           // the epilogue's z at the lane's two output columns (bf16)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *p, int bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, bytes, 0x00020000);
 }
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float x)
+{
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xf, true));
+}
+// Gated RMSNorm epilogue on the output row held by one wave, two columns per
+// lane (o0, o1 at the columns of z's two halves, weights w0, w1): the sum of
+// squares over the 16 lanes of a row (quad swaps, then the mirrored half and
+// row), then over the four rows.
+__device__ __forceinline__ uint32_t norm_pair(float o0, float o1, uint32_t z, float w0, float w1, float eps);
 
 // Sum over the four 16-lane rows of a wave, in every lane.
 __device__ __forceinline__ float rows_sum(float x)
@@ -268,6 +280,17 @@ __device__ __forceinline__ float rows_sum(float x)
     const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint32_t norm_pair(float o0, float o1, uint32_t z, float w0, float w1, float eps)
+{
+    float x = o0 * o0 + o1 * o1;
+    x = dpp_add<0xB1, 0xf>(x);    // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E, 0xf>(x);    // quad_perm [2,3,0,1]
+    x = dpp_add<0x141, 0xf>(x);   // row_half_mirror
+    x = dpp_add<0x140, 0xf>(x);   // row_mirror
+    const float r = norm_rinv(rows_sum(x), 128, eps);
+    return pack_bf16x2(o0 * r * w0 * norm_silu(bf16_lo(z)), o1 * r * w1 * norm_silu(bf16_hi(z)));
 }
 
 // Transposing reduction over the four 16-lane rows: given per-lane partials
@@ -302,8 +325,8 @@ __device__ __forceinline__ void s1_barrier()
 
 // GK: per-key decay gk given. FG: fused gates, beta and g formed in the
 // kernel from the logits and the raw gate input a. QN: q and k normalised in
-// the kernel.
-template <bool GK, bool FG, bool QN>
+// the kernel. NRM: gated RMSNorm epilogue on the outputs (norm_pair).
+template <bool GK, bool FG, bool QN, bool NRM>
 __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, int nheads)
 {
     using namespace s1;
@@ -322,6 +345,14 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
     const bf16_t *v = static_cast<const bf16_t *>(p.v);
     bf16_t *pool = static_cast<bf16_t *>(p.pool);
     bf16_t *out = static_cast<bf16_t *>(p.out);
+    // Gated RMSNorm epilogue (NRM): z of each head's row, w of the lane's columns.
+    const bf16_t *zsrc = static_cast<const bf16_t *>(p.norm_z);
+    float nw0 = 0.f, nw1 = 0.f;
+    if constexpr (NRM) {
+        const u32x2_t nwv = __builtin_amdgcn_raw_buffer_load_b64(brsrc(p.norm_w, DV * 4), (cg * 8 + lr * 2) * 4, 0, 0);
+        nw0 = __uint_as_float(nwv.x);
+        nw1 = __uint_as_float(nwv.y);
+    }
     // Optional inputs are read from a valid stand-in address and discarded,
     // so no load sits under a branch.
     const int32_t *nacc_src = p.nacc ? p.nacc : p.lens;
@@ -372,12 +403,15 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         H.v = __builtin_amdgcn_raw_buffer_load_b128(brsrc(v + (size_t)vh * DV, on ? DV * 2 : 0), cg * 16, 0, 0);
         if constexpr (GK)
             H.gk = __builtin_amdgcn_raw_buffer_load_b128(brsrc(p.gk + (size_t)vh * DK, on ? DK * 4 : 0), row0 * 4, 0, 0);
+        if constexpr (NRM)
+            H.z = __builtin_amdgcn_raw_buffer_load_b32(brsrc(zsrc + (size_t)vh * DV, on ? DV * 2 : 0), (cg * 8 + lr * 2) * 2, 0, 0);
     };
     // A skipped head still waits for its (empty) loads, so that every path
     // leaves the register sets settled: otherwise the compiler has to wait
     // for them where the paths meet, before the next prefetch is issued.
     auto settle = [&](const S1Head &H) __attribute__((always_inline)) {
         uint32_t x = H.k.x ^ H.q.x ^ H.v.x;
+        if constexpr (NRM) x ^= H.z;
 #pragma unroll
         for (int i = 0; i < NI; ++i) x ^= H.st[i].x ^ H.st[i].w;
         if constexpr (GK) x ^= H.gk.x;
@@ -509,8 +543,13 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         // delta of this lane row's two columns, then of all eight.
         const uint32_t vw = lr == 0 ? H.v.x : lr == 1 ? H.v.y : lr == 2 ? H.v.z : H.v.w;
         const float d0 = H.beta * (bf16_lo(vw) - u.x), d1 = H.beta * (bf16_hi(vw) - u.y);
-        if (j == 0)
-            *out_ptr(H) = pack_bf16x2(p.scale * fmaf(d0, kq, u.z), p.scale * fmaf(d1, kq, u.w));
+        if (j == 0) {
+            const float o0 = p.scale * fmaf(d0, kq, u.z), o1 = p.scale * fmaf(d1, kq, u.w);
+            if constexpr (NRM)
+                *out_ptr(H) = norm_pair(o0, o1, H.z, nw0, nw1, p.norm_eps);
+            else
+                *out_ptr(H) = pack_bf16x2(o0, o1);
+        }
         float e0[4], e1[4], dl[8];
         rows_gather(d0, e0);
         rows_gather(d1, e1);
@@ -591,11 +630,12 @@ struct MTTok {
     u32x4_t v;           // the lane's 8 columns of v (bf16)
     u32x4_t gk0, gk1;    // the lane's 8 rows of gk (f32)
     uint32_t beta, g;    // bf16 in the low half (beta or its logit; a); g as f32 bits
+    uint32_t z;          // the epilogue's z at the lane's two output columns (bf16)
     int w;               // the token's write slot
 };
 
-template <bool GK, bool FG, bool QN>
-__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(GK && (FG || QN) ? 3 : 4))) void decode_mt_kernel(DecodeParams p)
+template <bool GK, bool FG, bool QN, bool NRM>
+__global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK && (FG || QN)) || NRM ? 3 : 4))) void decode_mt_kernel(DecodeParams p)
 {
     using namespace mt;
     __shared__ float4 red[2][NW][64];
@@ -634,6 +674,14 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(GK 
     const float alog = FG ? __int_as_float(ld_const(reinterpret_cast<const int32_t *>(p.A_log), h)) : 0.f;
     const float dtb = FG ? __int_as_float(ld_const(reinterpret_cast<const int32_t *>(p.dt_bias), h)) : 0.f;
     const auto gkrs = brsrc(GK ? p.gk + vh * S * DK : nullptr, GK ? L * DK * 4 : 0);
+    // Gated RMSNorm epilogue (NRM): z of each token's row, w of the lane's columns.
+    const auto zrs = brsrc(NRM ? static_cast<const bf16_t *>(p.norm_z) + vh * S * DV : nullptr, NRM ? L * DV * 2 : 0);
+    float nw0 = 0.f, nw1 = 0.f;
+    if constexpr (NRM) {
+        const u32x2_t nwv = __builtin_amdgcn_raw_buffer_load_b64(brsrc(p.norm_w, DV * 4), (cg * 8 + lr * 2) * 4, 0, 0);
+        nw0 = __uint_as_float(nwv.x);
+        nw1 = __uint_as_float(nwv.y);
+    }
     auto ld_tok = [&](MTTok &T, int t) __attribute__((always_inline)) {
         T.k = __builtin_amdgcn_raw_buffer_load_b128(krs, (t * DK + row0) * 2, 0, 0);
         T.q = __builtin_amdgcn_raw_buffer_load_b128(qrs, (t * DK + row0) * 2, 0, 0);
@@ -647,6 +695,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(GK 
             T.g = __builtin_amdgcn_raw_buffer_load_b16(grs, t * 2, 0, 0);
         else
             T.g = __builtin_amdgcn_raw_buffer_load_b32(grs, t * 4, 0, 0);
+        if constexpr (NRM) T.z = __builtin_amdgcn_raw_buffer_load_b32(zrs, (t * DV + cg * 8 + lr * 2) * 2, 0, 0);
         T.w = ld_const(p.idx, (size_t)b * S + (t < S ? t : S - 1));
     };
 
@@ -761,7 +810,13 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu(GK 
         const float beta = FG ? gate_sigmoid(__uint_as_float(cur.beta << 16)) : __uint_as_float(cur.beta << 16);
         const uint32_t vw = lr == 0 ? cur.v.x : lr == 1 ? cur.v.y : lr == 2 ? cur.v.z : cur.v.w;
         const float d0 = beta * (bf16_lo(vw) - u.x), d1 = beta * (bf16_hi(vw) - u.y);
-        if (j == 0) optr[t * (DV / 2)] = pack_bf16x2(p.scale * fmaf(d0, kq, u.z), p.scale * fmaf(d1, kq, u.w));
+        if (j == 0) {
+            const float o0 = p.scale * fmaf(d0, kq, u.z), o1 = p.scale * fmaf(d1, kq, u.w);
+            if constexpr (NRM)
+                optr[t * (DV / 2)] = norm_pair(o0, o1, cur.z, nw0, nw1, p.norm_eps);
+            else
+                optr[t * (DV / 2)] = pack_bf16x2(o0, o1);
+        }
         float e0[4], e1[4], dl[8];
         rows_gather(d0, e0);
         rows_gather(d1, e1);
@@ -829,33 +884,45 @@ static hipError_t launch_typed(int Dk, int Dv, const DecodeParams &p, hipStream_
     return hipSuccess;
 }
 
-hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported)
+hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported,
+                         bool *norm_done)
 {
+    *norm_done = false;
     if (dtype == 1 && p.S == 1 && Dk == s1::DK && Dv == s1::DV) {
         *supported = true;
+        *norm_done = true;
         const int nheads = p.B * p.Nv;
         const dim3 grid((unsigned)(nheads < s1::GROUPS ? nheads : s1::GROUPS)), block(64 * s1::NW);
         DecodeParams pc = p;
         int nh = nheads;
         void *args[] = {&pc, &nh};
-        static const void *const fns[8] = {
-            (const void *)decode_s1_kernel<false, false, false>, (const void *)decode_s1_kernel<true, false, false>,
-            (const void *)decode_s1_kernel<false, true, false>,  (const void *)decode_s1_kernel<true, true, false>,
-            (const void *)decode_s1_kernel<false, false, true>,  (const void *)decode_s1_kernel<true, false, true>,
-            (const void *)decode_s1_kernel<false, true, true>,   (const void *)decode_s1_kernel<true, true, true>};
-        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0)];
+        static const void *const fns[16] = {
+            (const void *)decode_s1_kernel<false, false, false, false>, (const void *)decode_s1_kernel<true, false, false, false>,
+            (const void *)decode_s1_kernel<false, true, false, false>, (const void *)decode_s1_kernel<true, true, false, false>,
+            (const void *)decode_s1_kernel<false, false, true, false>, (const void *)decode_s1_kernel<true, false, true, false>,
+            (const void *)decode_s1_kernel<false, true, true, false>, (const void *)decode_s1_kernel<true, true, true, false>,
+            (const void *)decode_s1_kernel<false, false, false, true>, (const void *)decode_s1_kernel<true, false, false, true>,
+            (const void *)decode_s1_kernel<false, true, false, true>, (const void *)decode_s1_kernel<true, true, false, true>,
+            (const void *)decode_s1_kernel<false, false, true, true>, (const void *)decode_s1_kernel<true, false, true, true>,
+            (const void *)decode_s1_kernel<false, true, true, true>, (const void *)decode_s1_kernel<true, true, true, true>};
+        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
     if (dtype == 1 && p.S >= 2 && Dk == mt::DK && Dv == mt::DV) {
         *supported = true;
+        *norm_done = true;
         DecodeParams pc = p;
         void *args[] = {&pc};
-        static const void *const fns[8] = {
-            (const void *)decode_mt_kernel<false, false, false>, (const void *)decode_mt_kernel<true, false, false>,
-            (const void *)decode_mt_kernel<false, true, false>,  (const void *)decode_mt_kernel<true, true, false>,
-            (const void *)decode_mt_kernel<false, false, true>,  (const void *)decode_mt_kernel<true, false, true>,
-            (const void *)decode_mt_kernel<false, true, true>,   (const void *)decode_mt_kernel<true, true, true>};
-        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0)];
+        static const void *const fns[16] = {
+            (const void *)decode_mt_kernel<false, false, false, false>, (const void *)decode_mt_kernel<true, false, false, false>,
+            (const void *)decode_mt_kernel<false, true, false, false>, (const void *)decode_mt_kernel<true, true, false, false>,
+            (const void *)decode_mt_kernel<false, false, true, false>, (const void *)decode_mt_kernel<true, false, true, false>,
+            (const void *)decode_mt_kernel<false, true, true, false>, (const void *)decode_mt_kernel<true, true, true, false>,
+            (const void *)decode_mt_kernel<false, false, false, true>, (const void *)decode_mt_kernel<true, false, false, true>,
+            (const void *)decode_mt_kernel<false, true, false, true>, (const void *)decode_mt_kernel<true, true, false, true>,
+            (const void *)decode_mt_kernel<false, false, true, true>, (const void *)decode_mt_kernel<true, false, true, true>,
+            (const void *)decode_mt_kernel<false, true, true, true>, (const void *)decode_mt_kernel<true, true, true, true>};
+        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
         return hipLaunchKernel(fn, dim3((unsigned)(p.B * p.Nv)), dim3(64 * mt::NW), args, 0, s);
     }
     if (dtype == 1) return launch_typed<bf16_t>(Dk, Dv, p, s, supported);

@@ -40,12 +40,23 @@
  *    dimension before use (the blog post's use_qk_l2norm_in_kernel; deltanet.rs
  *    l2norm, with eps inside the square root). Otherwise callers pass
  *    normalised vectors.
+ *  - Gated RMSNorm output epilogue (optional, both calls): with norm_z and
+ *    norm_w given, every output row o = out[b, h, t, :] with t < L_b is
+ *    replaced by
+ *      o_j * w_j * silu(z_j) / sqrt(mean_j(o_j^2) + norm_eps),
+ *      silu(x) = x / (1 + exp(-x)),
+ *    formed in float32 from the unrounded o (inferencelayer deltanet.rs:
+ *    module header, the per-head gated RMSNorm of its step and chunk code and
+ *    of DN_STEP / DN_CHUNK). norm_z is (B, Nv, S, Dv) in dtype, norm_w (Dv)
+ *    float32 shared by all heads, norm_eps >= 0. A row whose o is all zeros
+ *    stays zero (also with norm_eps = 0); rows t >= L_b stay exact zeros and
+ *    z there is never read. The two pointers come together or not at all.
  *  - Return codes are produced on the host before anything is enqueued
  *    (except GDR_ERR_LAUNCH, from the launch itself). No value of g or gk is
  *    checked (the operator pages leave their sign unchecked on purpose).
  *  - Inputs and outputs must not overlap, except where stated.
- *  - q, k, v, the states, out and gk must be 16-byte aligned, and beta, g,
- *    beta_logits, gate_a, A_log and dt_bias 4-byte aligned
+ *  - q, k, v, the states, out, gk, norm_z and norm_w must be 16-byte aligned,
+ *    and beta, g, beta_logits, gate_a, A_log and dt_bias 4-byte aligned
  *    (GDR_ERR_UNSUPPORTED otherwise); torch allocations always are.
  */
 #ifndef GDR_H
@@ -113,9 +124,10 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  * Errors: GDR_ERR_NULL if a is NULL or q, k, v, state_pool, out,
  *   actual_seq_lengths or ssm_state_indices is NULL, beta is NULL without
  *   fused gates, or one of the four fused-gate pointers is given without the
- *   others (when B > 0); GDR_ERR_SHAPE if B < 0, S outside [1, 8], Nk, Nv,
- *   Dk, Dv or num_slots < 1, Nv % Nk != 0, num_state_indices != B*S, or beta
- *   or g is given together with fused gates; GDR_ERR_DTYPE;
+ *   others, or one of norm_z and norm_w without the other (when B > 0);
+ *   GDR_ERR_SHAPE if B < 0, S outside [1, 8], Nk, Nv, Dk, Dv or num_slots < 1,
+ *   Nv % Nk != 0, num_state_indices != B*S, beta or g is given together with
+ *   fused gates, or norm_eps < 0 (or NaN) with the epilogue; GDR_ERR_DTYPE;
  *   GDR_ERR_UNSUPPORTED; GDR_ERR_LAUNCH. B == 0 is a no-op.
  */
 typedef struct {
@@ -136,6 +148,10 @@ typedef struct {
     const void *gate_a;
     const float *A_log, *dt_bias;
     int32_t use_qk_l2norm;   /* 0: q and k used as given */
+    /* gated RMSNorm epilogue (see the conventions above), or NULL */
+    const void *norm_z;
+    const float *norm_w;
+    float norm_eps;
 } gdr_decode_args;
 
 GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
@@ -177,10 +193,12 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  *   (no workspace).
  * Errors: GDR_ERR_NULL if a, q, k, v, out or final_state is NULL, beta is
  *   NULL without fused gates, one of the four fused-gate pointers is given
- *   without the others, or workspace is NULL while a workspace is needed
- *   (when B > 0); GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1,
- *   Nv % Nk != 0, chunk_size < 1, workspace_bytes is below the needed size,
- *   or beta or g is given together with fused gates;
+ *   without the others, one of norm_z and norm_w without the other, or
+ *   workspace is NULL while a workspace is needed (when B > 0);
+ *   GDR_ERR_SHAPE if B < 0, S < 0, Nk, Nv, Dk, Dv < 1, Nv % Nk != 0,
+ *   chunk_size < 1, workspace_bytes is below the needed size, beta or g is
+ *   given together with fused gates, or norm_eps < 0 (or NaN) with the
+ *   epilogue;
  *   GDR_ERR_DTYPE; GDR_ERR_UNSUPPORTED (also for a misaligned pointer or
  *   S * D * 4 beyond 2^31 - 1); GDR_ERR_LAUNCH. B == 0 is a no-op.
  */
@@ -202,6 +220,10 @@ typedef struct {
     const void *gate_a;
     const float *A_log, *dt_bias;
     int32_t use_qk_l2norm;   /* 0: q and k used as given */
+    /* gated RMSNorm epilogue (see the conventions above), or NULL */
+    const void *norm_z;
+    const float *norm_w;
+    float norm_eps;
 } gdr_chunk_args;
 
 GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);
@@ -216,7 +238,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 3
+#define GDR_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

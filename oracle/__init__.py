@@ -15,12 +15,15 @@ Contents:
   gates                        the fused gates beta = sigmoid(b) and
                                g = -exp(A_log) softplus(a + dt_bias) (blog post's
                                layer code; deltanet.rs module header).
+  epilogue                     the gated RMSNorm o w silu(z) / sqrt(mean(o^2) + eps)
+                               applied to the output rows (deltanet.rs).
 
 Pins (tests/test_oracle_*.py) tie these to the pages: the worked examples of
 inferencelayer deltanet.rs's tests, brute force, store-then-recall with
 orthonormal keys, chunked == recurrent, g absent == alpha 1, pure decay,
 reduction to decayed linear attention, the per-step write identity, the Dk=1
-EMA, and contractivity; the gate functions against their closed forms. Parity unpinned: the speculative-decode slot rule
+EMA, and contractivity; the gate and epilogue functions against their closed
+forms. Parity unpinned: the speculative-decode slot rule
 (read slot idx[b*S + n_acc - 1], write slot idx[b*S + t]) beyond its special
 cases S = 1 and all tokens of a sequence on one slot.
 """

@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for seeding
-T_ALOG, T_DTBIAS, T_Q, T_K, T_V, T_A, T_B, T_GK, T_STATE, T_LENS, T_NACC, T_IDX = range(12)
+T_ALOG, T_DTBIAS, T_Q, T_K, T_V, T_A, T_B, T_GK, T_STATE, T_LENS, T_NACC, T_IDX, T_Z, T_W = range(14)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -191,6 +191,15 @@ def gate_inputs(base, B, Nv, S, dtype):
     a_log = _rng(base, T_ALOG).uniform(-2.0, 1.0, Nv).astype(np.float32)
     dt_bias = _rng(base, T_DTBIAS).uniform(-1.0, 1.0, Nv).astype(np.float32)
     return logits, a, a_log, dt_bias
+
+
+def norm_inputs(base, B, Nv, S, Dv, dtype):
+    """Inputs of the gated RMSNorm epilogue: the gate z ~ N(0, 1) per output
+    element (stored in the I/O dtype) and the weight w ~ U(0.5, 1.5) per column
+    (float32; a trained norm weight sits near 1). Returns (z, w)."""
+    z = _per_b(base, T_Z, B, lambda rng, b: _store(rng.standard_normal((Nv, S, Dv)), dtype))
+    w = _rng(base, T_W).uniform(0.5, 1.5, Dv).astype(np.float32)
+    return z, w
 
 
 def _poison(case: Case):

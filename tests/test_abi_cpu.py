@@ -84,7 +84,7 @@ def _chk(**kw):
 
 # Fused gates: the logits, a, A_log and dt_bias come together, in place of beta and g.
 _FUSED = dict(beta=None, beta_logits=FAKE, gate_a=FAKE, A_log=FAKE, dt_bias=FAKE)
-_GATE_CASES = [
+_OPTION_CASES = [
     (dict(_FUSED, beta=FAKE), gdr.GDR_ERR_SHAPE),
     (dict(_FUSED, g=FAKE), gdr.GDR_ERR_SHAPE),
     (dict(_FUSED, beta_logits=None), gdr.GDR_ERR_NULL),
@@ -97,6 +97,18 @@ _GATE_CASES = [
     (dict(_FUSED, beta_logits=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
     (dict(beta=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
     (dict(_FUSED, B=0, num_state_indices=0, q=None, out=None, workspace=None), gdr.GDR_OK),
+]
+# Gated RMSNorm epilogue: z and w together, eps a number >= 0, both 16-byte aligned.
+_NORM = dict(norm_z=FAKE, norm_w=FAKE, norm_eps=1e-6)
+_OPTION_CASES += [
+    (dict(norm_z=FAKE), gdr.GDR_ERR_NULL),
+    (dict(norm_w=FAKE), gdr.GDR_ERR_NULL),
+    (dict(_NORM, norm_eps=-1e-6), gdr.GDR_ERR_SHAPE),
+    (dict(_NORM, norm_eps=float("nan")), gdr.GDR_ERR_SHAPE),
+    (dict(_NORM, norm_z=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(_NORM, norm_w=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(_NORM, Dk=96), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(_NORM, B=0, num_state_indices=0, q=None, out=None, workspace=None), gdr.GDR_OK),
 ]
 
 
@@ -120,7 +132,7 @@ _GATE_CASES = [
     (dict(gk=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, num_state_indices=0, q=None, out=None), gdr.GDR_OK),
     (dict(beta=None), gdr.GDR_ERR_NULL),
-] + _GATE_CASES)
+] + _OPTION_CASES)
 def test_decode_validation(lib, kw, code):
     a = _dec(**kw)
     assert lib.gdr_decode(ctypes.byref(a), None) == code
@@ -145,7 +157,7 @@ def test_decode_validation(lib, kw, code):
     (dict(S=1 << 23), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, q=None, out=None, workspace=None), gdr.GDR_OK),
     (dict(beta=None), gdr.GDR_ERR_NULL),
-] + _GATE_CASES)
+] + _OPTION_CASES)
 def test_chunk_validation(lib, kw, code):
     a = _chk(**kw)
     assert lib.gdr_chunk(ctypes.byref(a), None) == code

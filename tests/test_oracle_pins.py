@@ -347,3 +347,39 @@ def test_l2norm_closed_forms():
     ny = np.sqrt((l2norm(r) ** 2).sum(-1))
     assert np.abs(ny - n / np.sqrt(n * n + e)).max() < 1e-15                   # norm closed form
     assert np.abs(l2norm(r) * np.sqrt(n * n + e)[:, None] - r).max() < 1e-12  # direction kept
+
+
+def test_silu_closed_forms():
+    from oracle.epilogue import silu
+    assert silu(np.array([0.0]))[0] == 0.0
+    assert abs(silu(np.array([math.log(3.0)]))[0] - 0.75 * math.log(3.0)) < 1e-15   # x sigmoid(x), sigmoid = 3/4
+    x = np.random.default_rng(6).uniform(-30, 30, 1000)
+    assert np.abs(silu(x) - silu(-x) - x).max() < 1e-13            # x (sigmoid(x) + sigmoid(-x)) = x
+    big = silu(np.array([-800.0, 800.0]))
+    assert big[0] == 0.0 and big[1] == 800.0                       # no overflow, no NaN
+
+
+def test_gated_rmsnorm_closed_forms():
+    from oracle.epilogue import gated_rmsnorm, silu
+    w = np.array([1.0, 2.0, 0.5, 1.5])
+    z = np.array([0.3, -1.2, 2.0, 0.0])
+    # A constant row c*1 with eps = 0 normalises to sign(c): the mean of the
+    # squares is c^2 (with their sum, 4c^2, the result would be halved).
+    for c in (3.0, -0.25):
+        out = gated_rmsnorm(np.full(4, c), z, w, 0.0)
+        assert np.abs(out - np.sign(c) * w * silu(z)).max() < 1e-15
+    # eps inside the square root: o = (3, 4, 0, 0), mean(o^2) = 25/4; with
+    # eps = 3/4 the factor is 1/sqrt(7).
+    o = np.array([3.0, 4.0, 0.0, 0.0])
+    out = gated_rmsnorm(o, z, w, 0.75)
+    assert np.abs(out - o / math.sqrt(7.0) * w * silu(z)).max() < 1e-15
+    # Scale invariance with eps = 0, and per-row independence over leading axes.
+    rng = np.random.default_rng(7)
+    rows = rng.standard_normal((3, 5, 16))
+    zz, ww = rng.standard_normal((3, 5, 16)), rng.uniform(0.5, 1.5, 16)
+    base = gated_rmsnorm(rows, zz, ww, 0.0)
+    assert np.abs(gated_rmsnorm(7.5 * rows, zz, ww, 0.0) - base).max() < 1e-13
+    assert np.abs(gated_rmsnorm(rows[1, 2], zz[1, 2], ww, 0.0) - base[1, 2]).max() < 1e-15
+    # Zero gate, zero output; an all-zero row stays zero even with eps = 0.
+    assert np.all(gated_rmsnorm(rows, np.zeros_like(zz), ww, 1e-6) == 0.0)
+    assert np.all(gated_rmsnorm(np.zeros(8), np.ones(8), np.ones(8), 0.0) == 0.0)
