@@ -17,6 +17,9 @@ Contents:
                                layer code; deltanet.rs module header).
   epilogue                     the gated RMSNorm o w silu(z) / sqrt(mean(o^2) + eps)
                                applied to the output rows (deltanet.rs).
+  conv                         the depthwise causal conv1d + SiLU ahead of the
+                               recurrence and its split into q, k, v (blog post's
+                               layer code; deltanet.rs conv ring).
 
 Pins (tests/test_oracle_*.py) tie these to the pages: the worked examples of
 inferencelayer deltanet.rs's tests, brute force, store-then-recall with

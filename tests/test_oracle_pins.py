@@ -383,3 +383,65 @@ def test_gated_rmsnorm_closed_forms():
     # Zero gate, zero output; an all-zero row stays zero even with eps = 0.
     assert np.all(gated_rmsnorm(rows, np.zeros_like(zz), ww, 1e-6) == 0.0)
     assert np.all(gated_rmsnorm(np.zeros(8), np.ones(8), np.ones(8), 0.0) == 0.0)
+
+
+def test_conv_closed_forms():
+    from oracle import conv
+    from oracle.epilogue import silu
+    rng = np.random.default_rng(9)
+    B, S, C, K = 2, 11, 6, 4
+    x = rng.standard_normal((B, S, C))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    # K = 1: a pointwise silu(w x + bias)
+    y, fin = conv.prefill(x, w[:, :1], bias, None, None)
+    assert np.abs(y - silu(x * w[:, 0] + bias)).max() < 1e-15 and fin.shape == (B, C, 0)
+    # impulse response: taps oldest first, so output t0 + m sees w[K - 1 - m]
+    imp = np.zeros((1, S, C))
+    imp[0, 3, 2] = 1.0
+    y, _ = conv.prefill(imp, w, None, None, None)
+    for t in range(S):
+        want = silu(np.array([w[2, K - 1 - (t - 3)] if 0 <= t - 3 < K else 0.0]))[0]
+        assert abs(y[0, t, 2] - want) < 1e-15
+    assert np.all(np.delete(y[0], 2, axis=1) == 0.0)
+    # the carried state alone (zero inputs): y_t = silu(sum_j w[j] init[j + t])
+    init = rng.standard_normal((1, C, K - 1))
+    y, fin = conv.prefill(np.zeros((1, 5, C)), w, None, init, None)
+    for t in range(5):
+        pre = sum(w[:, j] * init[0, :, j + t] for j in range(K - 1 - t)) if t < K - 1 else np.zeros(C)
+        assert np.abs(y[0, t] - silu(pre)).max() < 1e-14
+    assert np.all(fin == 0.0)                                  # the last K-1 inputs were zeros
+    # against numpy's full convolution (zero state): y_t = silu(bias + (x * w reversed)_t)
+    y, _ = conv.prefill(x, w, bias, None, None)
+    for c in range(C):
+        ref = np.convolve(x[1, :, c], w[c, ::-1])[:S] + bias[c]
+        assert np.abs(y[1, :, c] - silu(ref)).max() < 1e-13
+
+
+def test_conv_state_handoff_decode_and_split():
+    from oracle import conv
+    rng = np.random.default_rng(10)
+    B, S, C, K = 2, 13, 10, 4
+    x = rng.standard_normal((B, S, C))
+    w = rng.standard_normal((C, K))
+    bias = rng.standard_normal(C)
+    init = rng.standard_normal((B, C, K - 1))
+    y, fin = conv.prefill(x, w, bias, init, None)
+    # prefill of 5 then 8 tokens through the final state equals one call (bitwise)
+    y1, f1 = conv.prefill(x[:, :5], w, bias, init, None)
+    y2, f2 = conv.prefill(x[:, 5:], w, bias, f1, None)
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y) and np.array_equal(f2, fin)
+    # a length of 2 < K - 1: the final state mixes the initial state and the inputs
+    _, f = conv.prefill(x[:1], w, bias, init[:1], [2])
+    assert np.array_equal(f[0], np.concatenate([init[0, :, 2:], x[0, :2].T], axis=1))
+    # one-token decode steps through a one-slot pool equal the prefill (bitwise)
+    pool = init[1:2].copy()
+    for t in range(S):
+        yt, pool = conv.decode(x[1:2, t:t + 1], w, bias, pool, [1], [0], None)
+        assert np.array_equal(yt[0, 0], y[1, t])
+    assert np.array_equal(pool[0], fin[1])
+    # split: channel c of the (q | k | v) concatenation lands at its head and offset
+    Nk, Dk, Nv, Dv = 1, 2, 3, 2
+    yy = np.arange(1 * 4 * (2 * Nk * Dk + Nv * Dv), dtype=float).reshape(1, 4, -1)
+    q, k, v = conv.split(yy, Nk, Dk, Nv, Dv)
+    assert q[0, 0, 3, 1] == yy[0, 3, 1] and k[0, 0, 2, 0] == yy[0, 2, 2] and v[0, 2, 1, 1] == yy[0, 1, 4 + 2 * 2 + 1]
