@@ -58,6 +58,26 @@ class ChunkArgs(ctypes.Structure):
     ]
 
 
+class ConvPrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("Nk", ctypes.c_int32),
+        ("Nv", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("x", _vp), ("weight", _vp), ("bias", _vp), ("initial_state", _vp), ("final_state", _vp),
+        ("actual_seq_lengths", _vp), ("q", _vp), ("k", _vp), ("v", _vp),
+    ]
+
+
+class ConvDecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("B", ctypes.c_int32), ("S", ctypes.c_int32), ("Nk", ctypes.c_int32),
+        ("Nv", ctypes.c_int32), ("Dk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("num_slots", ctypes.c_int32), ("num_state_indices", ctypes.c_int64),
+        ("x", _vp), ("weight", _vp), ("bias", _vp), ("state_pool", _vp),
+        ("actual_seq_lengths", _vp), ("ssm_state_indices", _vp), ("num_accepted_tokens", _vp),
+        ("q", _vp), ("k", _vp), ("v", _vp),
+    ]
+
+
 _lib = None
 
 
@@ -79,6 +99,10 @@ def load_library(path: str = LIB_PATH):
     lib.gdr_status_string.argtypes = [ctypes.c_int]
     lib.gdr_abi_version.restype = ctypes.c_int32
     lib.gdr_abi_version.argtypes = []
+    lib.gdr_conv_prefill.restype = ctypes.c_int
+    lib.gdr_conv_prefill.argtypes = [ctypes.POINTER(ConvPrefillArgs), _vp]
+    lib.gdr_conv_decode.restype = ctypes.c_int
+    lib.gdr_conv_decode.argtypes = [ctypes.POINTER(ConvDecodeArgs), _vp]
     _lib = lib
     return lib
 
@@ -262,3 +286,71 @@ def chunk_workspace(a, dev):
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), n
     return ws
+
+
+def _conv_common(x, weight, bias, heads):
+    if x.dim() != 3:
+        raise ValueError("x must be (B, S, C)")
+    try:
+        Nk, Dk, Nv, Dv = (int(h) for h in heads)
+    except (TypeError, ValueError):
+        raise ValueError("heads must be (Nk, Dk, Nv, Dv)")
+    B, S, C = x.shape
+    if C != 2 * Nk * Dk + Nv * Dv:
+        raise ValueError(f"x has {C} channels, expected 2*Nk*Dk + Nv*Dv = {2 * Nk * Dk + Nv * Dv}")
+    dt = x.dtype
+    if dt not in _DT:
+        raise RuntimeError(f"unsupported dtype {dt}")
+    dev = x.device
+    if dev.type != "cuda":
+        raise RuntimeError("tensors must be on a GPU")
+    _need(x, "x", dt, dev)
+    if weight is None or weight.dim() != 2 or weight.shape[0] != C:
+        raise ValueError(f"weight must be ({C}, K)")
+    _need(weight, "weight", torch.float32, dev)
+    _need(bias, "bias", torch.float32, dev, (C,))
+    K = weight.shape[1]
+    q = torch.empty((B, Nk, S, Dk), dtype=dt, device=dev)
+    k = torch.empty((B, Nk, S, Dk), dtype=dt, device=dev)
+    v = torch.empty((B, Nv, S, Dv), dtype=dt, device=dev)
+    return B, S, C, K, Nk, Dk, Nv, Dv, dt, dev, q, k, v
+
+
+def gdr_conv_prefill(x, weight, heads, bias=None, initial_state=None, final_state=None, actual_seq_lengths=None):
+    """Depthwise causal conv1d + SiLU over x (B, S, C), split into q, k, v.
+
+    heads = (Nk, Dk, Nv, Dv) with C = 2*Nk*Dk + Nv*Dv; weight (C, K) and bias
+    (C,) float32; initial_state (B, C, K-1) or None (zeros); final_state
+    (B, C, K-1) or None (allocated; may be initial_state itself);
+    actual_seq_lengths (B,) int32 or None. Returns (q, k, v, final_state):
+    q, k (B, Nk, S, Dk) and v (B, Nv, S, Dv), zero past each length.
+    """
+    B, S, C, K, Nk, Dk, Nv, Dv, dt, dev, q, k, v = _conv_common(x, weight, bias, heads)
+    _need(initial_state, "initial_state", dt, dev, (B, C, K - 1))
+    if final_state is None:
+        final_state = torch.empty((B, C, K - 1), dtype=dt, device=dev)
+    _need(final_state, "final_state", dt, dev, (B, C, K - 1))
+    _need(actual_seq_lengths, "actual_seq_lengths", torch.int32, dev, (B,))
+    a = ConvPrefillArgs(_DT[dt], B, S, Nk, Nv, Dk, Dv, K, _ptr(x), _ptr(weight), _ptr(bias),
+                        _ptr(initial_state), _ptr(final_state), _ptr(actual_seq_lengths), _ptr(q), _ptr(k), _ptr(v))
+    _check(load_library().gdr_conv_prefill(ctypes.byref(a), _stream(dev)), "gdr_conv_prefill")
+    return q, k, v, final_state
+
+
+def gdr_conv_decode(x, weight, heads, state_pool, actual_seq_lengths, ssm_state_indices, bias=None,
+                    num_accepted_tokens=None):
+    """The conv1d + SiLU of up to 8 tokens per sequence over a pool of conv
+    states (slots, C, K-1), updated in place with gdr_decode's slot rule.
+    Returns (q, k, v, state_pool)."""
+    B, S, C, K, Nk, Dk, Nv, Dv, dt, dev, q, k, v = _conv_common(x, weight, bias, heads)
+    if state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != (C, K - 1):
+        raise ValueError(f"state_pool has shape {tuple(state_pool.shape)}, expected (slots, {C}, {K - 1})")
+    _need(state_pool, "state_pool", dt, dev)
+    _need(actual_seq_lengths, "actual_seq_lengths", torch.int32, dev, (B,))
+    _need(ssm_state_indices, "ssm_state_indices", torch.int32, dev)
+    _need(num_accepted_tokens, "num_accepted_tokens", torch.int32, dev, (B,))
+    a = ConvDecodeArgs(_DT[dt], B, S, Nk, Nv, Dk, Dv, K, state_pool.shape[0], ssm_state_indices.numel(),
+                       _ptr(x), _ptr(weight), _ptr(bias), _ptr(state_pool), _ptr(actual_seq_lengths),
+                       _ptr(ssm_state_indices), _ptr(num_accepted_tokens), _ptr(q), _ptr(k), _ptr(v))
+    _check(load_library().gdr_conv_decode(ctypes.byref(a), _stream(dev)), "gdr_conv_decode")
+    return q, k, v, state_pool

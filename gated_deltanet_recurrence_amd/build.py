@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_chunk.hip", "gdr_norm.hip"]
+SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_chunk.hip", "gdr_norm.hip", "gdr_conv.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

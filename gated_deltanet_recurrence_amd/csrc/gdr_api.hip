@@ -46,6 +46,35 @@ hipError_t launch_norm_pass(const Args *a, void *stream, bool *ok)
     return gdr::launch_norm(a->dtype, n, (hipStream_t)stream, ok);
 }
 
+// Shared checks of the two conv calls: sizes, then the pointers every call needs.
+template <typename Args>
+gdr_status check_conv(const Args *a, int max_S)
+{
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
+    if (a->B < 0 || a->S < 1 || a->S > max_S || a->Nk < 1 || a->Nv < 1 || a->Dk < 1 || a->Dv < 1 ||
+        a->Nv % a->Nk != 0 || a->Dk % 2 != 0 || a->Dv % 2 != 0 || a->K < 1 || a->K > 8)
+        return GDR_ERR_SHAPE;
+    if (a->B == 0) return GDR_OK;
+    if (!a->x || !a->weight || !a->q || !a->k || !a->v) return GDR_ERR_NULL;
+    const int64_t C = 2LL * a->Nk * a->Dk + (int64_t)a->Nv * a->Dv;
+    // 32-bit channel and grid arithmetic; 64-bit element offsets
+    if (C > (1LL << 30) || a->B > 65535 || (int64_t)a->S * C > (1LL << 40)) return GDR_ERR_UNSUPPORTED;
+    if (!aligned16(a->x) || !aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned4(a->weight) ||
+        !aligned4(a->bias))
+        return GDR_ERR_UNSUPPORTED;
+    return GDR_OK;
+}
+
+template <typename Args>
+void conv_params(const Args *a, gdr::ConvParams &p)
+{
+    p.x = a->x; p.w = a->weight; p.bias = a->bias;
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.B = a->B; p.S = a->S; p.Nk = a->Nk; p.Nv = a->Nv; p.Dk = a->Dk; p.Dv = a->Dv; p.K = a->K;
+    p.init = nullptr; p.fin = nullptr; p.pool = nullptr;
+    p.lens = nullptr; p.idx = nullptr; p.nacc = nullptr; p.slots = 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +189,39 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     bool ok = false;
     hipError_t e = gdr::launch_chunk(a->dtype, a->Dk, a->Dv, a->chunk_size, p, (hipStream_t)stream, &ok);
     if (e == hipSuccess && ok && a->norm_z) e = launch_norm_pass(a, stream, &ok);
+    return from_launch(e, ok);
+}
+
+gdr_status gdr_conv_prefill(const gdr_conv_prefill_args *a, void *stream)
+{
+    if (!a) return GDR_ERR_NULL;
+    const gdr_status cs = check_conv(a, 0x7fffffff);
+    if (cs != GDR_OK || a->B == 0) return cs;
+    if (!aligned16(a->initial_state) || !aligned16(a->final_state)) return GDR_ERR_UNSUPPORTED;
+    if ((a->S + 63) / 64 > 65535) return GDR_ERR_UNSUPPORTED;
+    gdr::ConvParams p;
+    conv_params(a, p);
+    p.init = a->initial_state; p.fin = a->final_state; p.lens = a->actual_seq_lengths;
+    bool ok = false;
+    hipError_t e = gdr::launch_conv_prefill(a->dtype, p, (hipStream_t)stream, &ok);
+    return from_launch(e, ok);
+}
+
+gdr_status gdr_conv_decode(const gdr_conv_decode_args *a, void *stream)
+{
+    if (!a) return GDR_ERR_NULL;
+    if (a->num_slots < 1 && a->B > 0) return GDR_ERR_SHAPE;
+    if (a->num_state_indices != (int64_t)a->B * a->S) return GDR_ERR_SHAPE;
+    const gdr_status cs = check_conv(a, 8);
+    if (cs != GDR_OK || a->B == 0) return cs;
+    if (!a->state_pool || !a->actual_seq_lengths || !a->ssm_state_indices) return GDR_ERR_NULL;
+    if (!aligned16(a->state_pool)) return GDR_ERR_UNSUPPORTED;
+    gdr::ConvParams p;
+    conv_params(a, p);
+    p.pool = a->state_pool; p.lens = a->actual_seq_lengths; p.idx = a->ssm_state_indices;
+    p.nacc = a->num_accepted_tokens; p.slots = a->num_slots;
+    bool ok = false;
+    hipError_t e = gdr::launch_conv_decode(a->dtype, p, (hipStream_t)stream, &ok);
     return from_launch(e, ok);
 }
 

@@ -61,6 +61,21 @@ struct NormParams {
 int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, int S);
 
 // Launchers: return hipSuccess or the launch error. dtype: 0 = f32, 1 = bf16.
+// Depthwise causal conv1d + SiLU with the q/k/v split (prefill: init/fin per
+// sequence; decode: pool with the recurrence's slot rule).
+struct ConvParams {
+    const void *x;
+    const float *w, *bias;
+    const void *init;
+    void *fin;
+    void *pool;
+    const int32_t *lens, *idx, *nacc;
+    void *q, *k, *v;
+    int32_t B, S, Nk, Nv, Dk, Dv, K, slots;
+};
+hipError_t launch_conv_prefill(int dtype, const ConvParams &p, hipStream_t s, bool *supported);
+hipError_t launch_conv_decode(int dtype, const ConvParams &p, hipStream_t s, bool *supported);
+
 // launch_decode sets *norm_done when the chosen kernel applied the epilogue itself.
 hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported,
                          bool *norm_done);

@@ -1,0 +1,237 @@
+// Depthwise causal conv1d + SiLU ahead of the recurrence, with the split of
+// its channels into q, k and v.
+//
+// Operation (the Gated DeltaNet blog post's layer code: causal_conv1d_fn and
+// causal_conv1d_update with the SiLU activation, then the split of the fused
+// projection; inferencelayer deltanet.rs: the conv ring of its step and chunk
+// code and DN_CONV), per channel c of the C = 2 Nk Dk + Nv Dv channels:
+//   y_t[c] = silu(bias[c] + sum_j w[c, j] x_{t-K+1+j}[c]),  taps oldest first,
+// with the inputs before the first token taken from the carried state (the
+// last K - 1 inputs, oldest first). y goes straight into the BNSD q, k, v the
+// recurrence kernels read, so the conv, the activation, the split and the
+// transpose are one pass over HBM.
+//
+// One thread per pair of adjacent channels (Dk and Dv are even, so a pair
+// never straddles a head): 4-byte (bf16) or 8-byte (float) accesses, adjacent
+// threads on adjacent pairs. Sums in float32.
+#include "gdr_common.h"
+
+namespace gdr {
+
+namespace {
+
+constexpr int CONV_THREADS = 256;
+constexpr int CONV_TB = 64;    // tokens per prefill workgroup
+constexpr int CONV_AHEAD = 8;  // input loads issued ahead of their use
+
+template <typename T> struct Pair2;
+template <> struct Pair2<bf16_t> {
+    static __device__ __forceinline__ float2 load(const bf16_t *p)
+    {
+        const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+        return make_float2(bf16_lo(u), bf16_hi(u));
+    }
+    static __device__ __forceinline__ void store(bf16_t *p, float2 v)
+    {
+        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(v.x, v.y);
+    }
+    static __device__ __forceinline__ float one(const bf16_t *p) { return to_f32(*p); }
+    static __device__ __forceinline__ void put(bf16_t *p, float v) { *p = from_f32<bf16_t>(v); }
+};
+template <> struct Pair2<float> {
+    static __device__ __forceinline__ float2 load(const float *p) { return *reinterpret_cast<const float2 *>(p); }
+    static __device__ __forceinline__ void store(float *p, float2 v) { *reinterpret_cast<float2 *>(p) = v; }
+    static __device__ __forceinline__ float one(const float *p) { return *p; }
+    static __device__ __forceinline__ void put(float *p, float v) { *p = v; }
+};
+
+// Where channel pair (c, c + 1) of token t of sequence b goes in q, k or v.
+template <typename T>
+__device__ __forceinline__ T *split_dst(const ConvParams &p, int b, int t, int c)
+{
+    const int nq = p.Nk * p.Dk;
+    if (c < nq)
+        return static_cast<T *>(p.q) + (((size_t)b * p.Nk + c / p.Dk) * p.S + t) * p.Dk + c % p.Dk;
+    if (c < 2 * nq) {
+        c -= nq;
+        return static_cast<T *>(p.k) + (((size_t)b * p.Nk + c / p.Dk) * p.S + t) * p.Dk + c % p.Dk;
+    }
+    c -= 2 * nq;
+    return static_cast<T *>(p.v) + (((size_t)b * p.Nv + c / p.Dv) * p.S + t) * p.Dv + c % p.Dv;
+}
+
+__device__ __forceinline__ float conv_silu(float u) { return u / (1.f + __expf(-u)); }
+
+// One token: window win[0..K-2] (oldest first) and input xin; returns y and
+// shifts xin into the window.
+template <int K>
+__device__ __forceinline__ float2 conv_step(float2 (&win)[K > 1 ? K - 1 : 1], float2 xin, const float (&w0)[K],
+                                            const float (&w1)[K], float2 bv)
+{
+    float2 acc = make_float2(fmaf(w0[K - 1], xin.x, bv.x), fmaf(w1[K - 1], xin.y, bv.y));
+#pragma unroll
+    for (int j = 0; j + 1 < K; ++j) {
+        acc.x = fmaf(w0[j], win[j].x, acc.x);
+        acc.y = fmaf(w1[j], win[j].y, acc.y);
+    }
+#pragma unroll
+    for (int j = 0; j + 2 < K; ++j) win[j] = win[j + 1];
+    if constexpr (K > 1) win[K - 2] = xin;
+    return make_float2(conv_silu(acc.x), conv_silu(acc.y));
+}
+
+template <int K>
+__device__ __forceinline__ void conv_weights(const ConvParams &p, int c, float (&w0)[K], float (&w1)[K], float2 &bv)
+{
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        w0[j] = p.w[(size_t)c * K + j];
+        w1[j] = p.w[(size_t)(c + 1) * K + j];
+    }
+    bv = p.bias ? make_float2(p.bias[c], p.bias[c + 1]) : make_float2(0.f, 0.f);
+}
+
+// Workgroup (channel pairs x, token block y, sequence z).
+template <typename T, int K>
+__global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p)
+{
+    constexpr int KW = K > 1 ? K - 1 : 1;
+    const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
+    const int c = 2 * (blockIdx.x * CONV_THREADS + threadIdx.x);
+    if (c >= C) return;
+    const int b = blockIdx.z, t0 = blockIdx.y * CONV_TB;
+    int L = p.lens ? ld_const(p.lens, b) : p.S;
+    L = L < 0 ? 0 : (L > p.S ? p.S : L);
+    const T *x = static_cast<const T *>(p.x) + (size_t)b * p.S * C + c;
+    const T *init = p.init ? static_cast<const T *>(p.init) + ((size_t)b * C + c) * (K - 1) : nullptr;
+    // input of token tau (tau < 0: the carried state; zeros without one)
+    auto input = [&](int tau) __attribute__((always_inline)) {
+        if (tau >= 0) return Pair2<T>::load(x + (size_t)tau * C);
+        if (!init) return make_float2(0.f, 0.f);
+        return make_float2(Pair2<T>::one(init + tau + K - 1), Pair2<T>::one(init + (K - 1) + tau + K - 1));
+    };
+    float w0[K], w1[K];
+    float2 bv;
+    conv_weights<K>(p, c, w0, w1, bv);
+    float2 win[KW];
+#pragma unroll
+    for (int j = 0; j + 1 < K; ++j) win[j] = t0 < L ? input(t0 - (K - 1) + j) : make_float2(0.f, 0.f);
+    const int tv = min(t0 + CONV_TB, L);
+    for (int ta = t0; ta < tv; ta += CONV_AHEAD) {
+        float2 xs[CONV_AHEAD];
+#pragma unroll
+        for (int i = 0; i < CONV_AHEAD; ++i) xs[i] = ta + i < tv ? Pair2<T>::load(x + (size_t)(ta + i) * C) : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < CONV_AHEAD; ++i)
+            if (ta + i < tv) Pair2<T>::store(split_dst<T>(p, b, ta + i, c), conv_step<K>(win, xs[i], w0, w1, bv));
+    }
+    // rows past the length: exact zeros
+    for (int t = max(t0, L); t < min(t0 + CONV_TB, p.S); ++t) Pair2<T>::store(split_dst<T>(p, b, t, c), make_float2(0.f, 0.f));
+    // The final state (the last K - 1 inputs) is written by the first token
+    // block, after its reads of the initial state, so it may alias it.
+    if (p.fin && blockIdx.y == 0 && K > 1) {
+        float2 f[KW];
+#pragma unroll
+        for (int j = 0; j + 1 < K; ++j) f[j] = input(L - (K - 1) + j);
+        T *fin = static_cast<T *>(p.fin) + ((size_t)b * C + c) * (K - 1);
+#pragma unroll
+        for (int j = 0; j + 1 < K; ++j) {
+            Pair2<T>::put(fin + j, f[j].x);
+            Pair2<T>::put(fin + (K - 1) + j, f[j].y);
+        }
+    }
+}
+
+// Workgroup (channel pairs x, sequence y); tokens in order, the state carried
+// in registers and stored after every valid token whose slot the next token
+// does not overwrite.
+template <typename T, int K>
+__global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvParams p)
+{
+    constexpr int KW = K > 1 ? K - 1 : 1;
+    const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
+    const int c = 2 * (blockIdx.x * CONV_THREADS + threadIdx.x);
+    if (c >= C) return;
+    const int b = blockIdx.y, S = p.S;
+    int L = ld_const(p.lens, b);
+    L = L < 0 ? 0 : (L > S ? S : L);
+    const int n = p.nacc ? ld_const(p.nacc, b) : L;
+    int r = -1;
+    if (L > 0 && n >= 1 && n <= S) r = ld_const(p.idx, (size_t)b * S + n - 1);
+    if (r < 0 || r >= p.slots) L = 0;   // skipped: zeros, no slot touched
+    const T *x = static_cast<const T *>(p.x) + (size_t)b * S * C + c;
+    T *pool = static_cast<T *>(p.pool);
+    float w0[K], w1[K];
+    float2 bv;
+    conv_weights<K>(p, c, w0, w1, bv);
+    float2 win[KW];
+    if (L > 0) {
+        const T *src = pool + ((size_t)r * C + c) * (K - 1);
+#pragma unroll
+        for (int j = 0; j + 1 < K; ++j) win[j] = make_float2(Pair2<T>::one(src + j), Pair2<T>::one(src + (K - 1) + j));
+    }
+    for (int t = 0; t < S; ++t) {
+        if (t >= L) {
+            Pair2<T>::store(split_dst<T>(p, b, t, c), make_float2(0.f, 0.f));
+            continue;
+        }
+        Pair2<T>::store(split_dst<T>(p, b, t, c), conv_step<K>(win, Pair2<T>::load(x + (size_t)t * C), w0, w1, bv));
+        const int s = ld_const(p.idx, (size_t)b * S + t);
+        const bool again = t + 1 < L && ld_const(p.idx, (size_t)b * S + t + 1) == s;
+        if (K > 1 && s >= 0 && s < p.slots && !again) {
+            T *dst = pool + ((size_t)s * C + c) * (K - 1);
+#pragma unroll
+            for (int j = 0; j + 1 < K; ++j) {
+                Pair2<T>::put(dst + j, win[j].x);
+                Pair2<T>::put(dst + (K - 1) + j, win[j].y);
+            }
+        }
+    }
+}
+
+template <template <typename, int> class Kern, typename T>
+const void *conv_fn(int K)
+{
+    switch (K) {
+    case 1: return (const void *)Kern<T, 1>::fn;
+    case 2: return (const void *)Kern<T, 2>::fn;
+    case 3: return (const void *)Kern<T, 3>::fn;
+    case 4: return (const void *)Kern<T, 4>::fn;
+    case 5: return (const void *)Kern<T, 5>::fn;
+    case 6: return (const void *)Kern<T, 6>::fn;
+    case 7: return (const void *)Kern<T, 7>::fn;
+    case 8: return (const void *)Kern<T, 8>::fn;
+    }
+    return nullptr;
+}
+template <typename T, int K> struct PrefillK { static constexpr auto fn = conv_prefill_kernel<T, K>; };
+template <typename T, int K> struct DecodeK { static constexpr auto fn = conv_decode_kernel<T, K>; };
+
+}  // namespace
+
+hipError_t launch_conv_prefill(int dtype, const ConvParams &p, hipStream_t s, bool *supported)
+{
+    const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
+    const void *fn = dtype == 1 ? conv_fn<PrefillK, bf16_t>(p.K) : conv_fn<PrefillK, float>(p.K);
+    *supported = fn != nullptr;
+    if (!fn) return hipSuccess;
+    ConvParams pc = p;
+    void *args[] = {&pc};
+    const dim3 grid((unsigned)((C / 2 + CONV_THREADS - 1) / CONV_THREADS), (unsigned)((p.S + CONV_TB - 1) / CONV_TB),
+                    (unsigned)p.B);
+    return hipLaunchKernel(fn, grid, dim3(CONV_THREADS), args, 0, s);
+}
+
+hipError_t launch_conv_decode(int dtype, const ConvParams &p, hipStream_t s, bool *supported)
+{
+    const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
+    const void *fn = dtype == 1 ? conv_fn<DecodeK, bf16_t>(p.K) : conv_fn<DecodeK, float>(p.K);
+    *supported = fn != nullptr;
+    if (!fn) return hipSuccess;
+    ConvParams pc = p;
+    void *args[] = {&pc};
+    const dim3 grid((unsigned)((C / 2 + CONV_THREADS - 1) / CONV_THREADS), (unsigned)p.B);
+    return hipLaunchKernel(fn, grid, dim3(CONV_THREADS), args, 0, s);
+}
+
+}  // namespace gdr

@@ -228,6 +228,75 @@ typedef struct {
 
 GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);
 
+/*
+ * Depthwise causal conv1d + SiLU ahead of the recurrence, with the split into
+ * q, k and v (the Gated DeltaNet blog post's layer code: causal_conv1d_fn /
+ * causal_conv1d_update with the SiLU activation, then torch.split; inferencelayer
+ * deltanet.rs: the conv ring of its step and chunk code and DN_CONV).
+ *
+ * The input x holds, per token, the C = 2*Nk*Dk + Nv*Dv channels of the fused
+ * projection in the order (q heads | k heads | v heads). For every channel c:
+ *   y_t[c] = silu(bias[c] + sum_{j=0}^{K-1} weight[c, j] * x_{t-K+1+j}[c]),
+ *   silu(u) = u / (1 + exp(-u)),
+ * taps oldest first, inputs before the first token taken from the carried
+ * state: the last K - 1 inputs of the channel, oldest first. y is written
+ * straight into q (B, Nk, S, Dk), k (B, Nk, S, Dk) and v (B, Nv, S, Dv):
+ * channel c < Nk*Dk is q[b, c / Dk, t, c % Dk], the next Nk*Dk are k likewise,
+ * the rest v. Rows t >= L_b of q, k and v are written as exact zeros, and
+ * x there is never read. The sums run in float32; outputs are rounded once.
+ *
+ * Sizes: B >= 0, S >= 1 (decode: S <= 8), Nk, Nv, Dk, Dv >= 1 with Nv % Nk == 0,
+ *   Dk and Dv even, 1 <= K <= 8. Tensors (device, row-major, dtype as for the
+ *   recurrence; weight and bias float32):
+ *   x (B, S, C); weight (C, K); bias (C) or NULL (zero).
+ * Errors: GDR_ERR_NULL for a missing required pointer (when B > 0);
+ *   GDR_ERR_SHAPE for sizes outside the ranges above or num_state_indices !=
+ *   B*S; GDR_ERR_DTYPE; GDR_ERR_UNSUPPORTED for a misaligned pointer (x, the
+ *   states and q, k, v 16-byte aligned; weight and bias 4-byte) or sizes beyond
+ *   the kernels' 32-bit offsets; GDR_ERR_LAUNCH. B == 0 is a no-op.
+ */
+
+/* Prefill: initial_state (B, C, K-1) or NULL (zeros); final_state (B, C, K-1)
+ * or NULL (not written) receives the last K-1 inputs after token L_b - 1
+ * (taking the initial state's where L_b < K - 1) and MAY alias initial_state;
+ * actual_seq_lengths (B) int32 or NULL (all S). */
+typedef struct {
+    int32_t dtype;
+    int32_t B, S, Nk, Nv, Dk, Dv, K;
+    const void *x;
+    const float *weight, *bias;
+    const void *initial_state;
+    void *final_state;
+    const int32_t *actual_seq_lengths;
+    void *q, *k, *v;
+} gdr_conv_prefill_args;
+
+GDR_API gdr_status gdr_conv_prefill(const gdr_conv_prefill_args *a, void *stream);
+
+/* Decode over an indexed pool of conv states, with the slot rule of
+ * gdr_decode: state_pool (num_slots, C, K-1) is read from slot
+ * ssm_state_indices[b*S + n_b - 1] (n_b = num_accepted_tokens[b], or L_b when
+ * NULL) and the state after valid token t is stored into slot
+ * ssm_state_indices[b*S + t]; a sequence with L_b == 0, n_b outside [1, S] or
+ * a read slot outside [0, num_slots) writes zeros and touches no slot, and a
+ * write slot outside that range skips that store only. A caller passes the
+ * same lengths, counts and indices as to gdr_decode. */
+typedef struct {
+    int32_t dtype;
+    int32_t B, S, Nk, Nv, Dk, Dv, K;
+    int32_t num_slots;
+    int64_t num_state_indices;
+    const void *x;
+    const float *weight, *bias;
+    void *state_pool;
+    const int32_t *actual_seq_lengths;
+    const int32_t *ssm_state_indices;
+    const int32_t *num_accepted_tokens;
+    void *q, *k, *v;
+} gdr_conv_decode_args;
+
+GDR_API gdr_status gdr_conv_decode(const gdr_conv_decode_args *a, void *stream);
+
 /* Bytes of workspace gdr_chunk needs for these arguments (0 if none; reads
  * dtype, B, Nv, S, Dk, Dv and chunk_size only); -1 if a is NULL. */
 GDR_API int64_t gdr_chunk_workspace_size(const gdr_chunk_args *a);
@@ -238,7 +307,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 4
+#define GDR_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

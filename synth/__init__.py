@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for seeding
-T_ALOG, T_DTBIAS, T_Q, T_K, T_V, T_A, T_B, T_GK, T_STATE, T_LENS, T_NACC, T_IDX, T_Z, T_W = range(14)
+T_ALOG, T_DTBIAS, T_Q, T_K, T_V, T_A, T_B, T_GK, T_STATE, T_LENS, T_NACC, T_IDX, T_Z, T_W, T_X, T_CW, T_CB, T_CS = range(18)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -200,6 +200,20 @@ def norm_inputs(base, B, Nv, S, Dv, dtype):
     z = _per_b(base, T_Z, B, lambda rng, b: _store(rng.standard_normal((Nv, S, Dv)), dtype))
     w = _rng(base, T_W).uniform(0.5, 1.5, Dv).astype(np.float32)
     return z, w
+
+
+def conv_inputs(base, B, S, C, K, dtype, slots=None):
+    """Inputs of the depthwise conv1d ahead of the recurrence: the fused
+    projection x ~ N(0, 1) per token and channel (the I/O dtype), weights
+    w ~ U(-1, 1) / sqrt(K) per channel and tap and bias ~ N(0, 0.1) per channel
+    (float32), and carried states ~ N(0, 1) in the I/O dtype: (B, C, K-1) per
+    sequence, or (slots, C, K-1) for a pool. Returns (x, w, bias, state)."""
+    x = _per_b(base, T_X, B, lambda rng, b: _store(rng.standard_normal((S, C)), dtype))
+    w = (_rng(base, T_CW).uniform(-1.0, 1.0, (C, K)) / np.sqrt(K)).astype(np.float32)
+    bias = (_rng(base, T_CB).standard_normal(C) * 0.1).astype(np.float32)
+    n = B if slots is None else slots
+    state = _store(_rng(base, T_CS).standard_normal((n, C, K - 1)), dtype)
+    return x, w, bias, state
 
 
 def _poison(case: Case):

@@ -25,7 +25,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = re.findall(r"GDR_API\s+[\w\s\*]+?\b(gdr_\w+)\s*\(", open(HEADER).read())
     assert set(names) == {"gdr_decode", "gdr_chunk", "gdr_chunk_workspace_size", "gdr_status_string",
-                          "gdr_abi_version"}
+                          "gdr_abi_version", "gdr_conv_prefill", "gdr_conv_decode"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", gbuild.LIB], capture_output=True, text=True).stdout
@@ -166,6 +166,65 @@ def test_chunk_validation(lib, kw, code):
 def test_null_args_struct(lib):
     assert lib.gdr_decode(None, None) == gdr.GDR_ERR_NULL
     assert lib.gdr_chunk(None, None) == gdr.GDR_ERR_NULL
+    assert lib.gdr_conv_prefill(None, None) == gdr.GDR_ERR_NULL
+    assert lib.gdr_conv_decode(None, None) == gdr.GDR_ERR_NULL
+
+
+# Depthwise conv: C = 2*Nk*Dk + Nv*Dv channels, K taps in [1, 8], even head sizes.
+def _convp(**kw):
+    a = dict(dtype=gdr.GDR_BF16, B=2, S=100, Nk=2, Nv=4, Dk=128, Dv=128, K=4, x=FAKE, weight=FAKE,
+             bias=None, initial_state=None, final_state=FAKE, actual_seq_lengths=None, q=FAKE, k=FAKE, v=FAKE)
+    a.update(kw)
+    return gdr.ConvPrefillArgs(**a)
+
+
+def _convd(**kw):
+    a = dict(dtype=gdr.GDR_BF16, B=2, S=2, Nk=2, Nv=4, Dk=128, Dv=128, K=4, num_slots=4, num_state_indices=4,
+             x=FAKE, weight=FAKE, bias=None, state_pool=FAKE, actual_seq_lengths=FAKE, ssm_state_indices=FAKE,
+             num_accepted_tokens=None, q=FAKE, k=FAKE, v=FAKE)
+    a.update(kw)
+    return gdr.ConvDecodeArgs(**a)
+
+
+_CONV_CASES = [
+    (dict(dtype=3), gdr.GDR_ERR_DTYPE),
+    (dict(K=0), gdr.GDR_ERR_SHAPE),
+    (dict(K=9), gdr.GDR_ERR_SHAPE),
+    (dict(Dk=127), gdr.GDR_ERR_SHAPE),
+    (dict(Dv=5), gdr.GDR_ERR_SHAPE),
+    (dict(Nv=3), gdr.GDR_ERR_SHAPE),
+    (dict(B=-1), gdr.GDR_ERR_SHAPE),
+    (dict(x=None), gdr.GDR_ERR_NULL),
+    (dict(weight=None), gdr.GDR_ERR_NULL),
+    (dict(v=None), gdr.GDR_ERR_NULL),
+    (dict(x=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(k=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(weight=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(bias=FAKE + 2), gdr.GDR_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("kw,code", _CONV_CASES + [
+    (dict(S=0), gdr.GDR_ERR_SHAPE),
+    (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(B=0, x=None, q=None), gdr.GDR_OK),
+])
+def test_conv_prefill_validation(lib, kw, code):
+    assert lib.gdr_conv_prefill(ctypes.byref(_convp(**kw)), None) == code
+
+
+@pytest.mark.parametrize("kw,code", _CONV_CASES + [
+    (dict(S=9, num_state_indices=18), gdr.GDR_ERR_SHAPE),
+    (dict(num_state_indices=3), gdr.GDR_ERR_SHAPE),
+    (dict(num_slots=0), gdr.GDR_ERR_SHAPE),
+    (dict(state_pool=None), gdr.GDR_ERR_NULL),
+    (dict(ssm_state_indices=None), gdr.GDR_ERR_NULL),
+    (dict(actual_seq_lengths=None), gdr.GDR_ERR_NULL),
+    (dict(state_pool=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(B=0, num_state_indices=0, x=None, q=None), gdr.GDR_OK),
+])
+def test_conv_decode_validation(lib, kw, code):
+    assert lib.gdr_conv_decode(ctypes.byref(_convd(**kw)), None) == code
 
 
 def test_binding_rejects_host_tensors(lib):
