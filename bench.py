@@ -12,6 +12,7 @@ exceeds the 256 MB last-level cache. Kernel time comes from HIP events
 recorded on the stream the kernels are launched on. Prints one JSON line.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -327,7 +328,7 @@ def main():
     ap.add_argument("--copies", type=int, default=8, help="decode pool copies rotated per step")
     ap.add_argument("--varlen", action="store_true", help="also time the varlen prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused", "norm"], default=None)
+    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused", "norm", "conv"], default=None)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -471,6 +472,59 @@ def main():
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls, c
         torch.cuda.empty_cache()
+
+    if args.only in (None, "conv"):
+        # The depthwise causal conv1d + SiLU ahead of the recurrence, at the
+        # chunked prefill and decode step sizes: C = 2 Nk Dk + Nv Dv = 8192
+        # channels, K = 4 taps, bf16. Bytes: x read and q, k, v written once,
+        # the carried states read and written, the weights and bias.
+        log("conv1d workloads")
+        lib = gdr.load_library()
+        K = 4
+        for name, B, S, slots in (("conv1d prefill", 4, 4096, None), ("conv1d decode step", 64, 1, 64)):
+            Nk, Dk, Nv, Dv = 16, 128, 32, 128
+            C = 2 * Nk * Dk + Nv * Dv
+            x, w, bias, st = synth.conv_inputs(505, B, S, C, K, "bf16", slots=slots)
+            calls, keep = [], []
+            for _ in range(2 if slots is None else args.copies):
+                t = dict(x=dev(x), w=dev(w), bias=dev(bias), st=dev(st),
+                         q=torch.empty((B, Nk, S, Dk), dtype=torch.bfloat16, device="cuda"),
+                         k=torch.empty((B, Nk, S, Dk), dtype=torch.bfloat16, device="cuda"),
+                         v=torch.empty((B, Nv, S, Dv), dtype=torch.bfloat16, device="cuda"))
+                if slots is None:
+                    t["fin"] = torch.empty_like(t["st"])
+                    a = gdr.ConvPrefillArgs(gdr.GDR_BF16, B, S, Nk, Nv, Dk, Dv, K, t["x"].data_ptr(), t["w"].data_ptr(),
+                                            t["bias"].data_ptr(), t["st"].data_ptr(), t["fin"].data_ptr(), None,
+                                            t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr())
+                    fn = lib.gdr_conv_prefill
+                else:
+                    t["lens"] = dev(np.ones(B, np.int32))
+                    t["idx"] = dev(np.random.default_rng(505).permutation(slots)[:B].astype(np.int32))
+                    a = gdr.ConvDecodeArgs(gdr.GDR_BF16, B, S, Nk, Nv, Dk, Dv, K, slots, B * S, t["x"].data_ptr(),
+                                           t["w"].data_ptr(), t["bias"].data_ptr(), t["st"].data_ptr(),
+                                           t["lens"].data_ptr(), t["idx"].data_ptr(), None,
+                                           t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr())
+                    fn = lib.gdr_conv_decode
+                keep.append((t, a))
+
+                def call(a=a, fn=fn):
+                    rc = fn(ctypes.byref(a), torch.cuda.current_stream().cuda_stream)
+                    if rc:
+                        raise RuntimeError(f"conv call failed: {rc}")
+                calls.append(call)
+            ms, wall, _ = time_calls(calls, args.steps if slots else max(10, args.steps // 8),
+                                     args.warmup if slots else max(2, args.warmup // 8), use_graph)
+            bytes_call = 2 * B * S * C * 2 + 2 * B * C * (K - 1) * 2 + C * (K + 1) * 4
+            gbs = bytes_call / (ms * 1e-3) / 1e9
+            secondary.append({"workload": f"{name}: B={B} S={S} C={C} (Nk=16 Dk=128 Nv=32 Dv=128) K={K} bf16, "
+                                          f"bias, carried state" + (f", {slots}-slot pool" if slots else ""),
+                              "tok_per_s": B * S / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": B * S,
+                              "roofline": {"kernel": "conv_prefill_kernel" if slots is None else "conv_decode_kernel",
+                                           "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                           "algorithmic_bytes_per_launch": bytes_call}})
+            del keep, calls
+            torch.cuda.empty_cache()
 
     prefill_sets = []
     if args.only in (None, "prefill"):

@@ -58,7 +58,10 @@ gdr_status check_conv(const Args *a, int max_S)
     if (!a->x || !a->weight || !a->q || !a->k || !a->v) return GDR_ERR_NULL;
     const int64_t C = 2LL * a->Nk * a->Dk + (int64_t)a->Nv * a->Dv;
     // 32-bit channel and grid arithmetic; 64-bit element offsets
-    if (C > (1LL << 30) || a->B > 65535 || (int64_t)a->S * C > (1LL << 40)) return GDR_ERR_UNSUPPORTED;
+    // 32-bit byte offsets within one sequence's inputs and one head's plane
+    // (the prefill reads whole 64-token blocks, up to S + 63)
+    if (C > (1LL << 30) || a->B > 65535 || ((int64_t)a->S + 64) * C * (a->dtype == GDR_F32 ? 4 : 2) > 0x7fffffffLL)
+        return GDR_ERR_UNSUPPORTED;
     if (!aligned16(a->x) || !aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned4(a->weight) ||
         !aligned4(a->bias))
         return GDR_ERR_UNSUPPORTED;

@@ -24,40 +24,65 @@ constexpr int CONV_THREADS = 256;
 constexpr int CONV_TB = 64;    // tokens per prefill workgroup
 constexpr int CONV_AHEAD = 8;  // input loads issued ahead of their use
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t conv_rsrc(const void *p, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// Two adjacent channels through a bounded buffer resource (byte offset off):
+// reads past the bound return zeros, stores past it are dropped, so neither
+// needs a branch.
 template <typename T> struct Pair2;
 template <> struct Pair2<bf16_t> {
-    static __device__ __forceinline__ float2 load(const bf16_t *p)
+    static __device__ __forceinline__ float2 load(__amdgpu_buffer_rsrc_t r, int off)
     {
-        const uint32_t u = *reinterpret_cast<const uint32_t *>(p);
+        const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
         return make_float2(bf16_lo(u), bf16_hi(u));
     }
-    static __device__ __forceinline__ void store(bf16_t *p, float2 v)
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float2 v)
     {
-        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(v.x, v.y);
+        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v.x, v.y), r, off, 0, 0);
     }
     static __device__ __forceinline__ float one(const bf16_t *p) { return to_f32(*p); }
     static __device__ __forceinline__ void put(bf16_t *p, float v) { *p = from_f32<bf16_t>(v); }
 };
 template <> struct Pair2<float> {
-    static __device__ __forceinline__ float2 load(const float *p) { return *reinterpret_cast<const float2 *>(p); }
-    static __device__ __forceinline__ void store(float *p, float2 v) { *reinterpret_cast<float2 *>(p) = v; }
+    static __device__ __forceinline__ float2 load(__amdgpu_buffer_rsrc_t r, int off)
+    {
+        const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        return make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
+    }
+    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float2 v)
+    {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(v.x), __float_as_uint(v.y)}, r, off, 0, 0);
+    }
     static __device__ __forceinline__ float one(const float *p) { return *p; }
     static __device__ __forceinline__ void put(float *p, float v) { *p = v; }
 };
 
-// Where channel pair (c, c + 1) of token t of sequence b goes in q, k or v.
+// Where channel pair (c, c + 1) of sequence b goes in q, k or v: the head's
+// plane of S rows of D elements, and the column d within a row.
 template <typename T>
-__device__ __forceinline__ T *split_dst(const ConvParams &p, int b, int t, int c)
+__device__ __forceinline__ T *split_dst(const ConvParams &p, int b, int c, int &D, int &d)
 {
     const int nq = p.Nk * p.Dk;
-    if (c < nq)
-        return static_cast<T *>(p.q) + (((size_t)b * p.Nk + c / p.Dk) * p.S + t) * p.Dk + c % p.Dk;
+    if (c < nq) {
+        D = p.Dk;
+        d = c % p.Dk;
+        return static_cast<T *>(p.q) + ((size_t)b * p.Nk + c / p.Dk) * p.S * p.Dk;
+    }
     if (c < 2 * nq) {
         c -= nq;
-        return static_cast<T *>(p.k) + (((size_t)b * p.Nk + c / p.Dk) * p.S + t) * p.Dk + c % p.Dk;
+        D = p.Dk;
+        d = c % p.Dk;
+        return static_cast<T *>(p.k) + ((size_t)b * p.Nk + c / p.Dk) * p.S * p.Dk;
     }
     c -= 2 * nq;
-    return static_cast<T *>(p.v) + (((size_t)b * p.Nv + c / p.Dv) * p.S + t) * p.Dv + c % p.Dv;
+    D = p.Dv;
+    d = c % p.Dv;
+    return static_cast<T *>(p.v) + ((size_t)b * p.Nv + c / p.Dv) * p.S * p.Dv;
 }
 
 __device__ __forceinline__ float conv_silu(float u) { return u / (1.f + __expf(-u)); }
@@ -91,42 +116,58 @@ __device__ __forceinline__ void conv_weights(const ConvParams &p, int c, float (
     bv = p.bias ? make_float2(p.bias[c], p.bias[c + 1]) : make_float2(0.f, 0.f);
 }
 
-// Workgroup (channel pairs x, token block y, sequence z).
+// Workgroup (channel pairs x, token block y, sequence z). Inputs are read
+// through a resource bounded by the sequence's valid tokens and outputs
+// written through one bounded by the head's plane: every token of the block
+// is loaded ahead and stored (zeros at t >= L) with no branch.
 template <typename T, int K>
 __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p)
 {
     constexpr int KW = K > 1 ? K - 1 : 1;
+    constexpr int E = sizeof(T);
     const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
     const int c = 2 * (blockIdx.x * CONV_THREADS + threadIdx.x);
     if (c >= C) return;
     const int b = blockIdx.z, t0 = blockIdx.y * CONV_TB;
     int L = p.lens ? ld_const(p.lens, b) : p.S;
     L = L < 0 ? 0 : (L > p.S ? p.S : L);
-    const T *x = static_cast<const T *>(p.x) + (size_t)b * p.S * C + c;
+    const T *xb = static_cast<const T *>(p.x) + (size_t)b * p.S * C;
+    const auto xrs = conv_rsrc(xb, (int64_t)L * C * E);
     const T *init = p.init ? static_cast<const T *>(p.init) + ((size_t)b * C + c) * (K - 1) : nullptr;
     // input of token tau (tau < 0: the carried state; zeros without one)
     auto input = [&](int tau) __attribute__((always_inline)) {
-        if (tau >= 0) return Pair2<T>::load(x + (size_t)tau * C);
+        if (tau >= 0) return Pair2<T>::load(xrs, (tau * C + c) * E);
         if (!init) return make_float2(0.f, 0.f);
         return make_float2(Pair2<T>::one(init + tau + K - 1), Pair2<T>::one(init + (K - 1) + tau + K - 1));
     };
     float w0[K], w1[K];
     float2 bv;
     conv_weights<K>(p, c, w0, w1, bv);
+    int D, d;
+    T *plane = split_dst<T>(p, b, c, D, d);
+    const auto ors = conv_rsrc(plane, (int64_t)p.S * D * E);
     float2 win[KW];
 #pragma unroll
-    for (int j = 0; j + 1 < K; ++j) win[j] = t0 < L ? input(t0 - (K - 1) + j) : make_float2(0.f, 0.f);
-    const int tv = min(t0 + CONV_TB, L);
-    for (int ta = t0; ta < tv; ta += CONV_AHEAD) {
-        float2 xs[CONV_AHEAD];
+    for (int j = 0; j + 1 < K; ++j) win[j] = input(t0 - (K - 1) + j);
+    // Two batches of CONV_AHEAD tokens in flight: the next one's loads are
+    // issued before the current one is computed.
+    float2 xs[2][CONV_AHEAD];
 #pragma unroll
-        for (int i = 0; i < CONV_AHEAD; ++i) xs[i] = ta + i < tv ? Pair2<T>::load(x + (size_t)(ta + i) * C) : make_float2(0.f, 0.f);
+    for (int i = 0; i < CONV_AHEAD; ++i) xs[0][i] = Pair2<T>::load(xrs, ((t0 + i) * C + c) * E);
 #pragma unroll
-        for (int i = 0; i < CONV_AHEAD; ++i)
-            if (ta + i < tv) Pair2<T>::store(split_dst<T>(p, b, ta + i, c), conv_step<K>(win, xs[i], w0, w1, bv));
+    for (int nb = 0; nb < CONV_TB / CONV_AHEAD; ++nb) {
+        const int ta = t0 + nb * CONV_AHEAD;
+        if (nb + 1 < CONV_TB / CONV_AHEAD) {
+#pragma unroll
+            for (int i = 0; i < CONV_AHEAD; ++i) xs[(nb + 1) & 1][i] = Pair2<T>::load(xrs, ((ta + CONV_AHEAD + i) * C + c) * E);
+        }
+#pragma unroll
+        for (int i = 0; i < CONV_AHEAD; ++i) {
+            float2 y = conv_step<K>(win, xs[nb & 1][i], w0, w1, bv);
+            if (ta + i >= L) y = make_float2(0.f, 0.f);   // rows past the length: exact zeros
+            Pair2<T>::store(ors, ((ta + i) * D + d) * E, y);
+        }
     }
-    // rows past the length: exact zeros
-    for (int t = max(t0, L); t < min(t0 + CONV_TB, p.S); ++t) Pair2<T>::store(split_dst<T>(p, b, t, c), make_float2(0.f, 0.f));
     // The final state (the last K - 1 inputs) is written by the first token
     // block, after its reads of the initial state, so it may alias it.
     if (p.fin && blockIdx.y == 0 && K > 1) {
@@ -142,13 +183,15 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p
     }
 }
 
-// Workgroup (channel pairs x, sequence y); tokens in order, the state carried
-// in registers and stored after every valid token whose slot the next token
-// does not overwrite.
+// Workgroup (channel pairs x, sequence y); the S <= 8 inputs are loaded first
+// (zeros past the valid tokens), then the tokens are applied in order, the
+// state carried in registers and stored after every valid token whose slot
+// the next token does not overwrite.
 template <typename T, int K>
 __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvParams p)
 {
     constexpr int KW = K > 1 ? K - 1 : 1;
+    constexpr int E = sizeof(T);
     const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
     const int c = 2 * (blockIdx.x * CONV_THREADS + threadIdx.x);
     if (c >= C) return;
@@ -159,23 +202,31 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvParams p)
     int r = -1;
     if (L > 0 && n >= 1 && n <= S) r = ld_const(p.idx, (size_t)b * S + n - 1);
     if (r < 0 || r >= p.slots) L = 0;   // skipped: zeros, no slot touched
-    const T *x = static_cast<const T *>(p.x) + (size_t)b * S * C + c;
+    const auto xrs = conv_rsrc(static_cast<const T *>(p.x) + (size_t)b * S * C, (int64_t)L * C * E);
+    float2 xs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xs[t] = Pair2<T>::load(xrs, (t * C + c) * E);
     T *pool = static_cast<T *>(p.pool);
     float w0[K], w1[K];
     float2 bv;
     conv_weights<K>(p, c, w0, w1, bv);
+    int D, d;
+    T *plane = split_dst<T>(p, b, c, D, d);
+    const auto ors = conv_rsrc(plane, (int64_t)S * D * E);
     float2 win[KW];
     if (L > 0) {
         const T *src = pool + ((size_t)r * C + c) * (K - 1);
 #pragma unroll
         for (int j = 0; j + 1 < K; ++j) win[j] = make_float2(Pair2<T>::one(src + j), Pair2<T>::one(src + (K - 1) + j));
     }
-    for (int t = 0; t < S; ++t) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        if (t >= S) break;
         if (t >= L) {
-            Pair2<T>::store(split_dst<T>(p, b, t, c), make_float2(0.f, 0.f));
+            Pair2<T>::store(ors, (t * D + d) * E, make_float2(0.f, 0.f));
             continue;
         }
-        Pair2<T>::store(split_dst<T>(p, b, t, c), conv_step<K>(win, Pair2<T>::load(x + (size_t)t * C), w0, w1, bv));
+        Pair2<T>::store(ors, (t * D + d) * E, conv_step<K>(win, xs[t], w0, w1, bv));
         const int s = ld_const(p.idx, (size_t)b * S + t);
         const bool again = t + 1 < L && ld_const(p.idx, (size_t)b * S + t + 1) == s;
         if (K > 1 && s >= 0 && s < p.slots && !again) {
