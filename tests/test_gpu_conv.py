@@ -64,6 +64,12 @@ def test_conv_prefill_fp32_and_taps():
     _prefill(2, 70, (1, 32, 2, 16), 8, "bf16", 814, lens=[70, 5])          # K = 8, a length below K - 1
 
 
+def test_conv_prefill_pair_kernel():
+    # head sizes even but not multiples of 8: two channels per thread
+    _prefill(2, 150, (1, 10, 2, 6), 3, "f32", 817, lens=[150, 65])
+    _prefill(2, 80, (2, 6, 2, 10), 4, "bf16", 818, lens=[80, 1])
+
+
 def test_conv_prefill_no_state_no_bias_and_alias():
     _prefill(2, 130, (2, 64, 2, 64), 4, "bf16", 815, init=False, bias=False)
     _prefill(3, 90, (2, 64, 4, 64), 4, "bf16", 816, lens=[90, 2, 64], alias=True)
