@@ -114,3 +114,14 @@ def test_conv_decode_multi_token():
     n_acc = np.minimum(rng.integers(1, S + 1, B), lens)
     _decode(B, S, (2, 128, 4, 128), 4, "bf16", 822, slots=B * S + 8, lens=lens, n_acc=n_acc, idx_mode="per_token")
     _decode(B, S, (1, 16, 2, 16), 3, "f32", 823, slots=B + 4, lens=lens, n_acc=None, idx_mode="per_seq")
+
+
+def test_conv_workloads_full_size():
+    # The launch configurations bench.py times: C = 2 Nk Dk + Nv Dv = 8192
+    # channels (Nk = 16, Dk = 128, Nv = 32, Dv = 128), K = 4, bf16, bias and
+    # carried state; prefill of 4 x 4096 tokens and a one-token step of 64
+    # sequences over a 64-slot pool. The conv oracle is cheap enough to run
+    # whole at these sizes.
+    heads = (16, 128, 32, 128)
+    _prefill(4, 4096, heads, 4, "bf16", 505, poison=False)
+    _decode(64, 1, heads, 4, "bf16", 505, slots=64, lens=[1] * 64, n_acc=None, idx_mode="per_seq")

@@ -26,7 +26,8 @@ import torch
 
 import synth
 from oracle.epilogue import gated_rmsnorm, silu
-from tests.gpu_util import TOL, assert_zero_rows, max_err, oracle_decode, oracle_prefill, raw_bits, say, to_dev, to_f64
+from tests.gpu_util import (TOL, assert_zero_rows, max_err, oracle_decode, oracle_prefill, oracle_units, raw_bits,
+                             say, to_dev, to_f64)
 from tests.test_gpu_fused_gates import _fused, _raw_qk
 import gated_deltanet_recurrence_amd as gdr
 
@@ -168,3 +169,39 @@ def test_epilogue_prefill_fp32():
     c = synth.prefill_case(B=2, Nk=1, Nv=2, S=100, Dk=32, Dv=32, dtype="f32", base=720, lens=[100, 37],
                            chunk=32, scale=0.3, init_std=0.1)
     _chunk(c, 720)
+
+
+def test_epilogue_decode_step_workload_full():
+    # the decode step workload at full size with bench.py's epilogue inputs
+    _decode(synth.config(2), 202)
+
+
+def test_epilogue_prefill_workload_full_sampled():
+    # the chunked prefill workload at full size with bench.py's epilogue
+    # inputs; the oracle on sampled (b, h) units
+    c = synth.config(4)
+    z, w = synth.norm_inputs(404, c.B, c.Nv, c.S, c.Dv, c.dtype)
+    say(f"gdr_chunk {c.dtype} B={c.B} S={c.S} Nv={c.Nv} epilogue, full size")
+
+    def call(norm):
+        return gdr.gdr_chunk(to_dev(c.q), to_dev(c.k), to_dev(c.v), to_dev(c.beta), initial_state=to_dev(c.state),
+                             actual_seq_lengths=to_dev(c.lens), g=to_dev(c.g), scale_value=c.scale,
+                             chunk_size=c.chunk, norm=norm)
+    plain, _ = call(None)
+    out, _ = call((to_dev(z), to_dev(w), EPS))
+    torch.cuda.synchronize()
+    units = [(0, 0), (1, 13), (2, 30), (3, 31), (3, 6)]
+    z64 = synth.widen(z, c.dtype)
+    L = c.valid_lengths()
+    for (b, h), (o_ref, _) in oracle_units(c, units).items():
+        n = int(L[b])
+        o = to_f64(out[b, h, :n])
+        e_row = np.abs(to_f64(plain[b, h, :n]) - o_ref).max(-1, keepdims=True)
+        assert float(e_row.max()) <= TOL[c.dtype], f"plain output unit {(b, h)}"
+        ref = gated_rmsnorm(o_ref, z64[b, h, :n], w, EPS)
+        r = 1.0 / np.sqrt((o_ref * o_ref).mean(-1, keepdims=True) + EPS)
+        gate = np.abs(w * silu(z64[b, h, :n]))
+        bound = TOL[c.dtype] + REL[c.dtype] * np.abs(ref) + e_row * r * (gate + np.abs(ref))
+        err = np.abs(o - ref)
+        assert np.all(err <= bound), f"unit {(b, h)}: worst {float((err - bound).max()):.3e} over the bound"
+    assert_zero_rows(out, L)
