@@ -333,7 +333,7 @@ def main():
                     help="first run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1"}))
         sys.exit(2)
     torch.cuda.init()
     gdr.load_library()
