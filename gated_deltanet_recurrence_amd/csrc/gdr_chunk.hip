@@ -484,6 +484,8 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 // Products that contract over tokens read K and V through LDS transpose
 // reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
+// FG: fused gates (raw a and beta logits in place of g and beta).
+template <bool FG>
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
     using namespace mk;
@@ -525,9 +527,12 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     const bf16_t *vb = static_cast<const bf16_t *>(p.v) + ((size_t)b * Nv + h) * S * DV + col0;
     const bf16_t *betab = static_cast<const bf16_t *>(p.beta) + ((size_t)b * Nv + h) * S;
     // g (float32), or with fused gates the raw input a (bf16)
-    const bool fg = p.gate_a != nullptr;
+    constexpr bool fg = FG;
     const void *gb = fg ? (const void *)(static_cast<const bf16_t *>(p.gate_a) + ((size_t)b * Nv + h) * S)
                         : (const void *)(p.g ? p.g + ((size_t)b * Nv + h) * S : nullptr);
+    // The fused gates' per-head parameters, read once: inside the chunk loop
+    // the stores to the outputs keep the compiler from hoisting them.
+    const float a_log = fg ? p.A_log[h] : 0.f, dt_b = fg ? p.dt_bias[h] : 0.f;
     bf16_t *ob = static_cast<bf16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV + col0;
     const bf16_t *ib = p.init ? static_cast<const bf16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
     bf16_t *fb = static_cast<bf16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
@@ -773,7 +778,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     if (fg) {
                         // Fused gates; tokens past the length are identity steps.
                         beta = lane < nv ? gate_sigmoid(beta) : 0.f;
-                        g = lane < nv ? gate_g(__uint_as_float(rg << 16), p.A_log[h], p.dt_bias[h]) : 0.f;
+                        g = lane < nv ? gate_g(__uint_as_float(rg << 16), a_log, dt_b) : 0.f;
                     }
                     const float gam2 = wave_prefix_sum(g) * 1.44269504088896340736f;
                     const float gamC2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam2), 63));
@@ -1054,12 +1059,14 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
             // Raise the dynamic-LDS limit once per process (first launch).
             static std::atomic<int> attr_done{0};
             if (!attr_done.load(std::memory_order_acquire)) {
-                hipError_t e = hipFuncSetAttribute((const void *)chunk_mfma_kernel,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, mk::LDS_BYTES);
-                if (e != hipSuccess) return e;
+                for (const void *f : {(const void *)chunk_mfma_kernel<false>, (const void *)chunk_mfma_kernel<true>}) {
+                    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::LDS_BYTES);
+                    if (e != hipSuccess) return e;
+                }
                 attr_done.store(1, std::memory_order_release);
             }
-            return hipLaunchKernel((const void *)chunk_mfma_kernel, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);
+            const void *fn = pc.gate_a ? (const void *)chunk_mfma_kernel<true> : (const void *)chunk_mfma_kernel<false>;
+            return hipLaunchKernel(fn, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);
         }
         *supported = false;
         return hipSuccess;
