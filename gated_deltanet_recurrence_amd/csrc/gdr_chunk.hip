@@ -269,55 +269,50 @@ __device__ __forceinline__ void wait_for(uint32_t *f, uint32_t target)
 // T = (I + A)^-1 of every chunk, ahead of the pass over the chunks: T depends
 // on k, beta and g of its chunk only, never on the state, so all chunks of
 // all sequences are independent. One wavefront per (sequence, value head,
-// chunk), with no exchange between wavefronts: the K operands come from
-// memory straight into registers, already in k-order, and every product
-// stays in the wave.
-//   Gram blocks G_00, G_11 (K_d K_d^T) and G_10 (K_1 K_0^T);
-//   -A_dd = -(diag(beta) G_dd) * exp(gamma_r - gamma_i) (strictly lower) and
-//   T_dd as the finite product (I - A)(I + A^2)(I + A^4)(I + A^8)(I + A^16)
-//   (A_dd is nilpotent of index 32), powers by squaring;
-//   T_10 = -T_11 A_10 T_00.
+// chunk), with no exchange between wavefronts.
+//
+// The solve is blocked forward substitution, which stays accurate however
+// close the keys of a chunk are to one another (repeated tokens give equal
+// keys); T itself is bounded there, but series forms of the inverse are not.
+//   1. Gram blocks G_00, G_11 (K_d K_d^T) and G_10 (K_1 K_0^T) on the matrix
+//      cores; A = strict_lower(diag(beta) K K^T * exp(gamma_r - gamma_i)).
+//   2. The four 16x16 diagonal blocks D_B = (I + A_BB)^-1 by forward
+//      substitution in float32, all four at once, one per 16-lane row of the
+//      wave: lane r of row B holds row r of A_BB and of D_B. Step m
+//      broadcasts row m of D_B (final by then) across the row and subtracts
+//      A[r, m] times it from every row r; rows r <= m have A[r, m] = 0.
+//   3. Two block merges. For a lower triangular matrix of two diagonal
+//      blocks with inverses D_0, D_1 and off-diagonal block A_10, the inverse
+//      has T_10 = -D_1 A_10 D_0 (block forward substitution), exactly. First
+//      inside each 32-block (16x16 blocks), then over the whole chunk:
+//      T_10 = -T_11 A_10 T_00 (32x32 blocks), on the matrix cores.
 // T is stored in result-register order, so that every store is 1 KB
 // contiguous: per chunk, block j (0: T_00, 1: T_11, 2: T_10) and k-step s hold
-// op8 of the block's 32x32 result, 16 bytes per lane: row r = c32 of the block
-// holds columns (k-order piece 2s + hh) at ((2j + s) * 64 + lane) * 16 bytes.
-// The block T_01 = 0 is neither written nor read; 6 KB of the 8 KB per chunk
-// are used.
+// op8 of D(T_j^T): row r = c32 of the block holds columns (k-order piece
+// 2s + hh) at ((2j + s) * 64 + lane) * 16 bytes. The block T_01 = 0 is neither
+// written nor read; 6 KB of the 8 KB per chunk are used.
 namespace tk {
 constexpr int WAVES = 4;                  // independent wavefronts per workgroup
 constexpr int CHUNK_ELEMS = 64 * 64;      // workspace elements per chunk
 }  // namespace tk
 
-// D((I + A_dd)^-1 ^T) for one 32x32 diagonal block, from its Gram block G
-// (D layout) and beta, gamma log2(e) of its rows (br, gr: the 16 rows this
-// lane holds) and of its column c32 (bc, gc).
-__device__ __forceinline__ f32x16_t diag_inverse_t(const f32x16_t &G, const float *br, const float *gr, float bc,
-                                                   float gc, int c32, int hh)
+// Value of lane m of the caller's 16-lane row, in every lane of the row
+// (DPP row_newbcast).
+template <int M>
+__device__ __forceinline__ float row_bcast(float x)
 {
-    // N = D(-A_dd), Nt = D(-A_dd^T), R = D((I - A_dd)^T). At each position
-    // only one of A_dd, A_dd^T can be nonzero (G is symmetric), so one
-    // exponential serves both.
-    f32x16_t N, Nt, R;
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + M, 0xf, 0xf, false));
+}
+// Steps M..14 of the forward substitution: x holds the lane's row of the
+// block's inverse, na the negated row of its strictly lower A.
+template <int M>
+__device__ __forceinline__ void fsub16(float (&x)[16], const float (&na)[16])
+{
+    if constexpr (M < 15) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int rl = drow(q, hh);
-        const bool below = c32 < rl;
-        const float dg = gr[q] - gc;
-        const float a = -__builtin_amdgcn_exp2f(below ? dg : -dg) * (below ? br[q] : bc) * G[q];
-        N[q] = below ? a : 0.f;
-        Nt[q] = rl < c32 ? a : 0.f;
-        R[q] = rl == c32 ? 1.f : Nt[q];
+        for (int j = 0; j <= M; ++j) x[j] = fmaf(na[M], row_bcast<M>(x[j]), x[j]);
+        fsub16<M + 1>(x, na);
     }
-    // R_{k+1}^T = R_k^T + (N^(2^k))^T R_k^T, powers by squaring.
-    f32x16_t M = prod(Nt, N, zero16()), Mt = prod(N, Nt, zero16());   // N^2
-    R = prod(M, R, R);
-    f32x16_t M2 = prod(Mt, M, zero16()), M2t = prod(M, Mt, zero16());  // N^4
-    R = prod(M2, R, R);
-    M = prod(M2t, M2, zero16());
-    Mt = prod(M2, M2t, zero16());                                     // N^8
-    R = prod(M, R, R);
-    M2 = prod(Mt, M, zero16());                                       // N^16
-    return prod(M2, R, R);
 }
 
 __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_t_kernel(ChunkParams p, int nchk, int units)
@@ -418,11 +413,97 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
         G1 = mfma32(kf[1][ks], kf[1][ks], G1);
         G10 = mfma32(kf[1][ks], kf[0][ks], G10);
     }
-    // A_10 (rows 32-63 of A against columns 0-31; no mask needed).
-    float br1[16], gr1[16];
-    rows4(bg, 32, br1);
-    rows4(gv, 32, gr1);
+
+    // Off-diagonal 16x16 block of each 32-block d (its rows 16-31 against
+    // columns 0-15) as the left operand of k-step 1: registers 8-15 of D(A_dd)
+    // in the lanes of columns 0-15, zero elsewhere.
+    bf16x8_t aoff[2];
     {
+        float br[16], gr[16];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            rows4(bg, 32 * d, br);
+            rows4(gv, 32 * d, gr);
+            const float gc = gv[32 * d + c32];
+            const f32x16_t &G = d ? G1 : G0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                aoff[d][e] = (__bf16)(c32 < 16 ? br[8 + e] * __builtin_amdgcn_exp2f(gr[8 + e] - gc) * G[8 + e] : 0.f);
+        }
+    }
+
+    // Rows of the 16x16 diagonal blocks, one per lane: after the swap, lane
+    // 32d + c holds row c of G_dd (symmetric), its columns drow(q, 0) in x0
+    // and drow(q, 1) in x1. Lane l is row r = l % 16 of block B = l / 16.
+    const int B = lane >> 4, r = lane & 15, sb = B & 1;
+    float x[16];
+    {
+        float na[16];
+        float x0[16], x1[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(G0[q]), __float_as_uint(G1[q]), false, false);
+            x0[q] = __uint_as_float(s[0]);
+            x1[q] = __uint_as_float(s[1]);
+        }
+        // Column j of the block is column 16 sb + j of the 32-block: register
+        // 8 sb + 4 (j / 8) + j % 4 of x0 (j % 8 < 4) or x1.
+        const float brow = bg[16 * B + r], grow = gv[16 * B + r];
+        float gcol[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 g4 = *reinterpret_cast<const float4 *>(gv + 16 * B + 4 * m);
+            gcol[4 * m] = g4.x; gcol[4 * m + 1] = g4.y; gcol[4 * m + 2] = g4.z; gcol[4 * m + 3] = g4.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int qa = 4 * (j >> 3) + (j & 3);
+            const float *src = ((j >> 2) & 1) ? x1 : x0;
+            const float gjr = sb ? src[8 + qa] : src[qa];
+            // Exponent selected before exp2: past the diagonal it could overflow.
+            const float ex = __builtin_amdgcn_exp2f(j < r ? grow - gcol[j] : -INFINITY);
+            na[j] = -(brow * ex * gjr);
+            x[j] = j == r ? 1.f : 0.f;
+        }
+        fsub16<0>(x, na);
+    }
+    // D(D_dd^T) for the 32-block d (block diagonal of the two 16x16
+    // inverses): lane (hh, c32) holds row c32 at columns drow(q, hh). Each
+    // lane forms the hh = 0 and hh = 1 halves of its own row, and the swap
+    // sends them to the lanes of 32-block 0 (R0) and 1 (R1).
+    f32x16_t R0, R1;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const bool own = (q >> 3) == sb;
+        const float p0 = own ? x[8 * ((q >> 2) & 1) + (q & 3)] : 0.f;
+        const float p1 = own ? x[8 * ((q >> 2) & 1) + 4 + (q & 3)] : 0.f;
+        const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+        R0[q] = __uint_as_float(s[0]);
+        R1[q] = __uint_as_float(s[1]);
+    }
+    bf16x8_t eye[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
+    // Merge inside each 32-block: T_dd^T = D_dd^T - D_dd^T Aoff^T D_dd^T.
+    // Y = Aoff^T D_dd^T has nonzero rows 0-15 only (k-step 0 of the next
+    // product), Aoff nonzero rows 16-31 only (k-step 1 of this one); the left
+    // factor D_dd (not transposed) comes from D_dd^T and the identity.
+    auto merge16 = [&](f32x16_t &R, const bf16x8_t &ao) __attribute__((always_inline)) {
+        const f32x16_t Y = mfma32(ao, op8(R, 1), zero16());
+        const f32x16_t E = -mfma32(op8(R, 0), eye[0], zero16());
+        R = mfma32(op8(E, 0), op8(Y, 0), R);
+    };
+    merge16(R0, aoff[0]);
+    merge16(R1, aoff[1]);
+
+    // A_10 (rows 32-63 of A against columns 0-31; no mask needed).
+    {
+        float br1[16], gr1[16];
+        rows4(bg, 32, br1);
+        rows4(gv, 32, gr1);
         const float gi = gv[c32];
 #pragma unroll
         for (int q = 0; q < 16; ++q) G10[q] *= br1[q] * __builtin_amdgcn_exp2f(gr1[q] - gi);
@@ -432,27 +513,13 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     auto put = [&](int j, int s, bf16x8_t v) __attribute__((always_inline)) {
         *reinterpret_cast<bf16x8_t *>(tw + ((2 * j + s) * 64 + lane) * 16) = v;
     };
-    // T_11, then Z = -(T_11 A_10)^T = -A_10^T T_11^T.
-    const f32x16_t R1 = diag_inverse_t(G1, br1, gr1, bg[32 + c32], gv[32 + c32], c32, hh);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) put(1, s, op8(R1, s));
-    f32x16_t Z = -prod(G10, R1, zero16());
-    // The two inverses run one after the other (G_00 is held back until T_11
-    // is done): overlapped, they would double the registers in use.
-    asm volatile("" : "+v"(G0) : "v"(Z[0]));
-    // T_00, then T_10^T = T_00^T Z with D(T_00) from D(T_00^T) and the identity.
-    float br0[16], gr0[16];
-    rows4(bg, 0, br0);
-    rows4(gv, 0, gr0);
-    const f32x16_t R0 = diag_inverse_t(G0, br0, gr0, bg[c32], gv[c32], c32, hh);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) put(0, s, op8(R0, s));
-    bf16x8_t eye[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
+    for (int s = 0; s < 2; ++s) {
+        put(0, s, op8(R0, s));
+        put(1, s, op8(R1, s));
+    }
+    // T_10^T = -T_00^T A_10^T T_11^T, with D(T_00) from D(T_00^T) and the identity.
+    const f32x16_t Z = -prod(G10, R1, zero16());
     f32x16_t T0 = mfma32(op8(R0, 0), eye[0], zero16());
     T0 = mfma32(op8(R0, 1), eye[1], T0);
     const f32x16_t T10 = prod(T0, Z, zero16());

@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for seeding
-T_ALOG, T_DTBIAS, T_Q, T_K, T_V, T_A, T_B, T_GK, T_STATE, T_LENS, T_NACC, T_IDX, T_Z, T_W, T_X, T_CW, T_CB, T_CS = range(18)
+T_ALOG, T_DTBIAS, T_Q, T_K, T_V, T_A, T_B, T_GK, T_STATE, T_LENS, T_NACC, T_IDX, T_Z, T_W, T_X, T_CW, T_CB, T_CS, T_KDIR = range(19)
 
 BF16_NAN = np.uint16(0x7FC0)
 
@@ -152,6 +152,26 @@ def _unit_vectors(base, tid, B, N, S, D, dtype):
     return _per_b(base, tid, B, fn)
 
 
+def _correlated_keys(base, B, N, S, D, dtype, mix):
+    """Keys that resemble one another, as repeated or related tokens give after
+    a short convolution. mix = m in [0, 1]: k_t = l2norm(m sqrt(D) c + (1 - m) n_t)
+    with one unit direction c per (b, key head) and n_t ~ N(0, I); the mean
+    cosine between two keys is about m^2 / (m^2 + (1 - m)^2), and m = 1 makes
+    every key equal. mix = ("vocab", n): every key is one of n unit vectors
+    per (b, key head), drawn at random per token (runs of repeated tokens)."""
+    def fn(rng, b):
+        if isinstance(mix, tuple) and mix[0] == "vocab":
+            voc = _l2n(rng.standard_normal((N, mix[1], D), dtype=np.float32))
+            pick = rng.integers(0, mix[1], (N, S))
+            x = np.take_along_axis(voc, pick[:, :, None], axis=1)
+        else:
+            m = np.float32(mix)
+            c = _l2n(rng.standard_normal((N, 1, D), dtype=np.float32)) * np.float32(math.sqrt(D))
+            x = m * c + (np.float32(1) - m) * rng.standard_normal((N, S, D), dtype=np.float32)
+        return _store(_l2n(np.ascontiguousarray(x, dtype=np.float32)), dtype)
+    return _per_b(base, T_KDIR, B, fn)
+
+
 def _normals(base, tid, B, shape, dtype, std=1.0):
     def fn(rng, b):
         x = rng.standard_normal(shape, dtype=np.float32)
@@ -236,12 +256,16 @@ def _poison(case: Case):
 
 def prefill_case(*, B, Nk, Nv, S, Dk, Dv, dtype="bf16", base=404, gate="gate",
                  init_std: Optional[float] = 0.02, lens=None, chunk=64, scale=None,
-                 poison_pad=False) -> Case:
+                 poison_pad=False, key_mix=None) -> Case:
     """Chunked-prefill inputs. gate: "gate" (the -exp(A_log)*softplus recipe),
     ("uniform", lo, hi), or None (g absent, alpha = 1). lens: None (all S),
-    ("uniform", lo, hi) seeded draws, or an explicit int sequence."""
+    ("uniform", lo, hi) seeded draws, or an explicit int sequence. key_mix:
+    None (independent keys) or correlated keys (see _correlated_keys)."""
     q = _unit_vectors(base, T_Q, B, Nk, S, Dk, dtype)
-    k = _unit_vectors(base, T_K, B, Nk, S, Dk, dtype)
+    if key_mix is None:
+        k = _unit_vectors(base, T_K, B, Nk, S, Dk, dtype)
+    else:
+        k = _correlated_keys(base, B, Nk, S, Dk, dtype, key_mix)
     v = _normals(base, T_V, B, (Nv, S, Dv), dtype)
     beta = _betas(base, B, Nv, S, dtype)
     if gate is None:
