@@ -21,7 +21,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-GDR_OK, GDR_ERR_NULL, GDR_ERR_SHAPE, GDR_ERR_DTYPE, GDR_ERR_UNSUPPORTED, GDR_ERR_LAUNCH = range(6)
+GDR_OK, GDR_ERR_NULL, GDR_ERR_SHAPE, GDR_ERR_DTYPE, GDR_ERR_UNSUPPORTED, GDR_ERR_LAUNCH, GDR_ERR_SCRATCH_LIMIT = range(7)
+GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
 GDR_F32, GDR_BF16 = 0, 1
 
 _vp = ctypes.c_void_p
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH):
     lib.gdr_decode.argtypes = [ctypes.POINTER(DecodeArgs), _vp]
     lib.gdr_chunk.restype = ctypes.c_int
     lib.gdr_chunk.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
+    lib.gdr_chunk_noalloc.restype = ctypes.c_int
+    lib.gdr_chunk_noalloc.argtypes = [ctypes.POINTER(ChunkArgs), _vp]
     lib.gdr_chunk_workspace_size.restype = ctypes.c_int64
     lib.gdr_chunk_workspace_size.argtypes = [ctypes.POINTER(ChunkArgs)]
     lib.gdr_status_string.restype = ctypes.c_char_p
@@ -111,7 +114,7 @@ def _check(rc: int, what: str):
     if rc == GDR_OK:
         return
     msg = f"{what}: {load_library().gdr_status_string(rc).decode()} (status {rc})"
-    if rc == GDR_ERR_SHAPE:
+    if rc in (GDR_ERR_SHAPE, GDR_ERR_SCRATCH_LIMIT):
         raise ValueError(msg)
     raise RuntimeError(msg)
 
@@ -233,15 +236,10 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     return out, state_pool
 
 
-def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
-              chunk_size=64, out=None, final_state=None, gates=None, use_qk_l2norm=False, norm=None):
-    """Chunked prefill. Returns (out, final_state).
-
-    q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); initial_state
-    (B, Nv, Dk, Dv) or None — one dtype; g (B, Nv, S) float32 or None;
-    actual_seq_lengths (B,) int32 or None. final_state may be initial_state
-    itself (updated in place). gates, use_qk_l2norm, norm: as for gdr_decode.
-    """
+def _chunk_args(q, k, v, beta, initial_state, actual_seq_lengths, g, scale_value, chunk_size, out,
+                final_state, gates, use_qk_l2norm, norm):
+    """Checks and marshals gdr_chunk's arguments; returns (ChunkArgs, out,
+    final_state, device), the workspace fields left empty."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, N, S, D)")
     B, Nk, S, Dk = k.shape
@@ -268,10 +266,36 @@ def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None
                   _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(initial_state),
                   _ptr(actual_seq_lengths), float(scale_value), _ptr(out), _ptr(final_state),
                   None, 0, *fused, int(bool(use_qk_l2norm)), *_norm(norm, dt, dev, B, Nv, S, Dv))
+    return a, out, final_state, dev
+
+
+def gdr_chunk(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
+              chunk_size=64, out=None, final_state=None, gates=None, use_qk_l2norm=False, norm=None):
+    """Chunked prefill. Returns (out, final_state).
+
+    q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); initial_state
+    (B, Nv, Dk, Dv) or None — one dtype; g (B, Nv, S) float32 or None;
+    actual_seq_lengths (B,) int32 or None. final_state may be initial_state
+    itself (updated in place). gates, use_qk_l2norm, norm: as for gdr_decode.
+    """
+    a, out, final_state, dev = _chunk_args(q, k, v, beta, initial_state, actual_seq_lengths, g, scale_value,
+                                           chunk_size, out, final_state, gates, use_qk_l2norm, norm)
     lib = load_library()
     ws = chunk_workspace(a, dev)
     _check(lib.gdr_chunk(ctypes.byref(a), _stream(dev)), "gdr_chunk")
     del ws   # stream-ordered reuse by the caching allocator is safe after the enqueue
+    return out, final_state
+
+
+def gdr_chunk_noalloc(q, k, v, beta, initial_state=None, actual_seq_lengths=None, g=None, scale_value=1.0,
+                      chunk_size=64, out=None, final_state=None, gates=None, use_qk_l2norm=False, norm=None):
+    """gdr_chunk through the allocation-free entry point: the library's fixed
+    per-GPU scratch array replaces the workspace (GDR_NOALLOC_SCRATCH_BYTES;
+    calls beyond it raise ValueError). Pass out and final_state to keep the
+    call free of allocations; calls that overlap on one GPU race on the array."""
+    a, out, final_state, dev = _chunk_args(q, k, v, beta, initial_state, actual_seq_lengths, g, scale_value,
+                                           chunk_size, out, final_state, gates, use_qk_l2norm, norm)
+    _check(load_library().gdr_chunk_noalloc(ctypes.byref(a), _stream(dev)), "gdr_chunk_noalloc")
     return out, final_state
 
 

@@ -1,10 +1,40 @@
 // C ABI of libgdr.so: argument validation on the host, kernel selection and
 // launch on the caller's stream. The operations and argument contracts are
 // documented in include/gdr.h.
+#include <mutex>
+
 #include "gdr.h"
 #include "gdr_common.h"
 
+// Scratch of gdr_chunk_noalloc: one array per GPU, held until the process
+// ends. In host code its name is only a stand-in for the device symbol; its
+// device address is resolved per device with hipGetSymbolAddress and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+void *scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device, once resolved
+
+// Device address of `scratch` on the current device, resolved on first use.
+hipError_t scratch_address(void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
 
 bool aligned16(const void *p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
@@ -93,6 +123,7 @@ const char *gdr_status_string(gdr_status s)
     case GDR_ERR_DTYPE: return "unknown element type";
     case GDR_ERR_UNSUPPORTED: return "no kernel for these head sizes, chunk size or alignment";
     case GDR_ERR_LAUNCH: return "kernel launch failed";
+    case GDR_ERR_SCRATCH_LIMIT: return "the call needs more scratch than the allocation-free entry point holds";
     }
     return "unknown status";
 }
@@ -147,7 +178,13 @@ int64_t gdr_chunk_workspace_size(const gdr_chunk_args *a)
     return gdr::chunk_workspace_bytes(a->dtype, a->Dk, a->Dv, a->chunk_size, a->B, a->Nv, a->S);
 }
 
-gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
+}  // extern "C"
+
+namespace {
+
+// gdr_chunk and gdr_chunk_noalloc: the same validation and launch; the
+// scratch is the caller's workspace, or (noalloc) the library's array.
+gdr_status chunk_call(const gdr_chunk_args *a, void *stream, bool noalloc)
 {
     if (!a) return GDR_ERR_NULL;
     if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
@@ -161,7 +198,7 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     const gdr_status ns = check_norm(a->norm_z, a->norm_w, a->norm_eps);
     if (ns != GDR_OK) return ns;
     if (!aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned16(a->out) ||
-        !aligned16(a->initial_state) || !aligned16(a->final_state) || !aligned16(a->workspace) ||
+        !aligned16(a->initial_state) || !aligned16(a->final_state) || (!noalloc && !aligned16(a->workspace)) ||
         !aligned16(a->norm_z) || !aligned16(a->norm_w) ||
         !aligned4(a->beta) || !aligned4(a->beta_logits) || !aligned4(a->gate_a) || !aligned4(a->g) ||
         !aligned4(a->A_log) || !aligned4(a->dt_bias))
@@ -172,8 +209,15 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
         return GDR_ERR_UNSUPPORTED;
     if (a->norm_z && !gdr::norm_supported(a->Dv, a->B, a->Nv, a->S)) return GDR_ERR_UNSUPPORTED;
     const int64_t need = gdr_chunk_workspace_size(a);
-    if (need > 0 && !a->workspace) return GDR_ERR_NULL;
-    if (need > a->workspace_bytes) return GDR_ERR_SHAPE;
+    void *work = a->workspace;
+    if (noalloc) {
+        if (need > GDR_NOALLOC_SCRATCH_BYTES) return GDR_ERR_SCRATCH_LIMIT;
+        work = nullptr;
+        if (need > 0 && scratch_address(&work) != hipSuccess) return GDR_ERR_LAUNCH;
+    } else {
+        if (need > 0 && !a->workspace) return GDR_ERR_NULL;
+        if (need > a->workspace_bytes) return GDR_ERR_SHAPE;
+    }
 
     gdr::ChunkParams p;
     p.q = a->q; p.k = a->k; p.v = a->v;
@@ -186,7 +230,7 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     p.lens = a->actual_seq_lengths;
     p.out = a->out;
     p.fin = a->final_state;
-    p.work = a->workspace;
+    p.work = work;
     p.scale = a->scale_value;
     p.B = a->B; p.Nk = a->Nk; p.Nv = a->Nv; p.S = a->S;
     bool ok = false;
@@ -194,6 +238,14 @@ gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream)
     if (e == hipSuccess && ok && a->norm_z) e = launch_norm_pass(a, stream, &ok);
     return from_launch(e, ok);
 }
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream) { return chunk_call(a, stream, false); }
+
+gdr_status gdr_chunk_noalloc(const gdr_chunk_args *a, void *stream) { return chunk_call(a, stream, true); }
 
 gdr_status gdr_conv_prefill(const gdr_conv_prefill_args *a, void *stream)
 {

@@ -81,7 +81,9 @@ typedef enum {
     GDR_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes (ValueError) */
     GDR_ERR_DTYPE = 3,       /* unknown dtype code                              */
     GDR_ERR_UNSUPPORTED = 4, /* head sizes / chunk size with no compiled kernel */
-    GDR_ERR_LAUNCH = 5       /* the kernel launch failed (RuntimeError)         */
+    GDR_ERR_LAUNCH = 5,      /* the kernel launch failed (RuntimeError)         */
+    GDR_ERR_SCRATCH_LIMIT = 6 /* gdr_chunk_noalloc: the call needs more scratch
+                                than the library's fixed array holds (ValueError) */
 } gdr_status;
 
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
@@ -297,6 +299,31 @@ typedef struct {
 
 GDR_API gdr_status gdr_conv_decode(const gdr_conv_decode_args *a, void *stream);
 
+/*
+ * gdr_chunk for callers that cannot allocate device memory: code under HIP
+ * graph (stream) capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, semantics and results as gdr_chunk, except that
+ * workspace and workspace_bytes are ignored: the scratch that gdr_chunk takes
+ * from the caller comes from a fixed device array inside the library,
+ * GDR_NOALLOC_SCRATCH_BYTES per GPU, reserved when the library's code is
+ * loaded on that GPU and held until the process ends. The call itself
+ * allocates nothing. Its first call on a device (the device current on the
+ * calling thread, which must own `stream`) resolves the array's address once.
+ * Every call on one GPU uses that GPU's single array, which keeps whatever the
+ * last call left in it (nothing in it needs to start at zero): calls that can
+ * run at the same time on one GPU — on different streams, or from host
+ * threads without ordering between them — race on it and must not overlap;
+ * calls ordered on one stream are safe.
+ * Limit: gdr_chunk_workspace_size(a) <= GDR_NOALLOC_SCRATCH_BYTES; for the
+ * bf16 128/128 path that is B * Nv * ceil(S / 64) <= 8192 chunks (the chunked
+ * prefill of B = 4, Nv = 32, S = 4096 exactly). f32 calls need no scratch.
+ * Errors: those of gdr_chunk (without its workspace checks), then
+ *   GDR_ERR_SCRATCH_LIMIT beyond the limit (nothing is enqueued), and
+ *   GDR_ERR_LAUNCH if the array's address cannot be resolved.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES (64LL << 20)
+GDR_API gdr_status gdr_chunk_noalloc(const gdr_chunk_args *a, void *stream);
+
 /* Bytes of workspace gdr_chunk needs for these arguments (0 if none; reads
  * dtype, B, Nv, S, Dk, Dv and chunk_size only); -1 if a is NULL. */
 GDR_API int64_t gdr_chunk_workspace_size(const gdr_chunk_args *a);
@@ -307,7 +334,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 5
+#define GDR_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

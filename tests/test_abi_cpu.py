@@ -24,8 +24,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = re.findall(r"GDR_API\s+[\w\s\*]+?\b(gdr_\w+)\s*\(", open(HEADER).read())
-    assert set(names) == {"gdr_decode", "gdr_chunk", "gdr_chunk_workspace_size", "gdr_status_string",
-                          "gdr_abi_version", "gdr_conv_prefill", "gdr_conv_decode"}
+    assert set(names) == {"gdr_decode", "gdr_chunk", "gdr_chunk_noalloc", "gdr_chunk_workspace_size",
+                          "gdr_status_string", "gdr_abi_version", "gdr_conv_prefill", "gdr_conv_decode"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", gbuild.LIB], capture_output=True, text=True).stdout
@@ -36,8 +36,8 @@ def test_exports_every_declared_symbol(lib):
 def test_abi_version_and_status_strings(lib):
     m = re.search(r"#define GDR_ABI_VERSION (\d+)", open(HEADER).read())
     assert lib.gdr_abi_version() == int(m.group(1))
-    for code in range(6):
-        assert lib.gdr_status_string(code)
+    for code in range(7):
+        assert lib.gdr_status_string(code) and lib.gdr_status_string(code) != b"unknown status"
     assert lib.gdr_status_string(99) == b"unknown status"
 
 
@@ -163,9 +163,40 @@ def test_chunk_validation(lib, kw, code):
     assert lib.gdr_chunk(ctypes.byref(a), None) == code
 
 
+# The allocation-free entry point validates like gdr_chunk, ignores the
+# workspace fields, and refuses calls whose scratch exceeds its fixed array
+# (B * Nv * ceil(S / 64) chunks of 8 KiB on the bf16 path) before touching
+# the device. Calls that pass validation are GPU tests.
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=-1), gdr.GDR_ERR_DTYPE),
+    (dict(Nv=5), gdr.GDR_ERR_SHAPE),
+    (dict(k=None), gdr.GDR_ERR_NULL),
+    (dict(beta=None), gdr.GDR_ERR_NULL),
+    (dict(chunk_size=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(B=0, q=None, out=None), gdr.GDR_OK),
+    (dict(B=4, Nk=16, Nv=32, S=4097), gdr.GDR_ERR_SCRATCH_LIMIT),
+    (dict(B=4, Nk=16, Nv=32, S=4097, workspace=FAKE + 8, workspace_bytes=0), gdr.GDR_ERR_SCRATCH_LIMIT),
+    (dict(B=16, Nk=16, Nv=64, S=16384), gdr.GDR_ERR_SCRATCH_LIMIT),
+])
+def test_chunk_noalloc_validation(lib, kw, code):
+    a = _chk(**kw)
+    assert lib.gdr_chunk_noalloc(ctypes.byref(a), None) == code
+
+
+def test_noalloc_limit_is_the_header_constant(lib):
+    m = re.search(r"#define GDR_NOALLOC_SCRATCH_BYTES \((\d+)LL << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    assert limit == gdr.GDR_NOALLOC_SCRATCH_BYTES
+    # the chunked prefill workload's scratch fits exactly; one chunk more does not
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(B=4, Nk=16, Nv=32, S=4096))) == limit
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(B=4, Nk=16, Nv=32, S=4097))) > limit
+
+
 def test_null_args_struct(lib):
     assert lib.gdr_decode(None, None) == gdr.GDR_ERR_NULL
     assert lib.gdr_chunk(None, None) == gdr.GDR_ERR_NULL
+    assert lib.gdr_chunk_noalloc(None, None) == gdr.GDR_ERR_NULL
     assert lib.gdr_conv_prefill(None, None) == gdr.GDR_ERR_NULL
     assert lib.gdr_conv_decode(None, None) == gdr.GDR_ERR_NULL
 
