@@ -301,7 +301,7 @@ constexpr int CHUNK_ELEMS = 64 * 64;      // workspace elements per chunk
 template <int M>
 __device__ __forceinline__ float row_bcast(float x)
 {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + M, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + M, 0xf, 0xf, true));
 }
 // Steps M..14 of the forward substitution: x holds the lane's row of the
 // block's inverse, na the negated row of its strictly lower A.
@@ -426,9 +426,11 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
             rows4(gv, 32 * d, gr);
             const float gc = gv[32 * d + c32];
             const f32x16_t &G = d ? G1 : G0;
+            // -inf as the exponent, not a select of the product: the select
+            // compiles to one branch per element, each with its own wait.
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                aoff[d][e] = (__bf16)(c32 < 16 ? br[8 + e] * __builtin_amdgcn_exp2f(gr[8 + e] - gc) * G[8 + e] : 0.f);
+                aoff[d][e] = (__bf16)(br[8 + e] * __builtin_amdgcn_exp2f(c32 < 16 ? gr[8 + e] - gc : -INFINITY) * G[8 + e]);
         }
     }
 
