@@ -3,8 +3,9 @@
 Headline: decode tokens/s on the decode step workload (B=64, Nk=16, Nv=32,
 S=1, Dk=Dv=128, bf16, 64-slot pool), with the state traffic as a fraction of
 HBM peak. Secondary entries: speculative decode (B=128, S=4, per-key gate),
-chunked prefill (B=4, S=4096, Nv=32) and, with --varlen, varlen prefill
-without decay (B=16, S<=16384, Nv=64), each with its roofline.
+chunked prefill (B=4, S=4096, Nv=32) and varlen prefill without decay (B=16,
+S<=16384, Nv=64), each with its roofline and an oracle CPU baseline, plus the
+fused-gate, epilogue and conv1d variants.
 
 A step is one call of the operator over one batch. Inputs sit in HBM before
 the timed region; decode rotates over enough pool copies that the working set
@@ -54,6 +55,8 @@ CSRC = os.path.join(ROOT, "gated_deltanet_recurrence_amd", "csrc")
 KERNEL_SOURCES = {
     "decode": ["gdr_decode.hip", "gdr_common.h"],
     "chunk": ["gdr_chunk.hip", "gdr_common.h"],
+    "chunk+norm": ["gdr_chunk.hip", "gdr_norm.hip", "gdr_common.h"],
+    "conv": ["gdr_conv.hip", "gdr_common.h"],
 }
 
 
@@ -65,19 +68,30 @@ def source_hash(kind):
     return h.hexdigest()
 
 
-def measured_traffic(profile, kind):
+def measured_traffic(profile, kind, entry=None):
     """HBM bytes per launch recorded in a profiles/ summary, or None when the
-    summary is missing or was taken from a different kernel source."""
+    summary is missing or was taken from a different kernel source. A summary
+    covering several launches labels each figure, as
+    "traffic bytes per launch [entry]: `N`", and records the hash of every
+    kind of source it covers as "kernel source sha256 [kind]: `H`"."""
     path = os.path.join(ROOT, "profiles", profile)
     try:
         text = open(path).read()
     except OSError:
         return None
+    tag = "" if entry is None else re.escape(f" [{entry}]")
+    m_bytes = re.search(r"traffic bytes per launch" + tag + r": `(\d+)`", text)
+    hashes = dict(re.findall(r"kernel source sha256 \[([\w+]+)\]: `([0-9a-f]{64})`", text))
     m_hash = re.search(r"kernel source sha256: `([0-9a-f]{64})`", text)
-    m_bytes = re.search(r"traffic bytes per launch: `(\d+)`", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(kind):
+    h = hashes.get(kind, m_hash.group(1) if m_hash else None)
+    if not m_bytes or h != source_hash(kind):
         return None
     return int(m_bytes.group(1))
+
+
+FUSED_PROFILE = "fused_gates_decode_step_and_chunked_prefill.txt"
+NORM_PROFILE = "epilogue_kernels_decode_step_and_chunked_prefill.txt"
+CONV_PROFILE = "conv_kernels_prefill_and_decode_step.txt"
 
 
 # ---------------------------------------------------------------------------
@@ -295,7 +309,7 @@ def cpu_baseline_decode(c, budget_s):
     return res
 
 
-def cpu_baseline_prefill(c, units, name):
+def cpu_baseline_prefill(c, units, name, whole):
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     rep = c.Nv // c.Nk
@@ -313,9 +327,13 @@ def cpu_baseline_prefill(c, units, name):
     with ThreadPoolExecutor(nt) as ex:
         list(ex.map(lambda w: oracle.sequence(w[0], w[1], w[2], w[3], g=w[4], state=w[5], scale=c.scale), work))
     el = time.perf_counter() - t0
-    tok = int(sum(L[b] for b, _ in units))
-    return {"value": tok / el, "unit": "token-heads/s", "cores": nt, "kind": "oracle",
-            "sample": f"{len(units)} (sequence, head) units of the {name} workload, {tok} token-heads, {el:.1f} s"}
+    th = int(sum(L[b] for b, _ in units))
+    # tok/s counts a token once for all Nv value heads, as the GPU figure does
+    what = "all" if whole else f"{len(units)} of the {c.B * c.Nv}"
+    return {"value": th / c.Nv / el, "unit": "tok/s", "cores": nt, "kind": "oracle",
+            "token_heads_per_s": th / el,
+            "sample": f"{what} (sequence, value head) units of the {name} workload: {th} token-heads "
+                      f"({th / c.Nv:.0f} tokens of {c.Nv} heads), {el:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -326,7 +344,6 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--copies", type=int, default=8, help="decode pool copies rotated per step")
-    ap.add_argument("--varlen", action="store_true", help="also time the varlen prefill workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused", "norm", "conv"], default=None)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -415,7 +432,8 @@ def main():
                           "state_GBps": state_b / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "decode_s1_kernel (fused gates)", "bound": "hbm", "achieved": gbs,
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                       "traffic": None, "algorithmic_bytes_per_launch": bytes_call}})
+                                       "traffic": measured_traffic(FUSED_PROFILE, "decode", "decode step"),
+                                       "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls
         torch.cuda.empty_cache()
         log("chunked prefill workload, fused gates")
@@ -430,7 +448,8 @@ def main():
                           "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel (fused gates)", "bound": "mfma",
                                        "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                                       "frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                                       "traffic": measured_traffic(FUSED_PROFILE, "chunk", "chunked prefill"),
                                        "algorithmic_flops_per_launch": flops,
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls, c
@@ -452,7 +471,8 @@ def main():
                           "state_GBps": state_b / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "decode_s1_kernel (epilogue in the kernel)", "bound": "hbm",
                                        "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                       "traffic": None, "algorithmic_bytes_per_launch": bytes_call}})
+                                       "traffic": measured_traffic(NORM_PROFILE, "decode", "decode step"),
+                                       "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls
         torch.cuda.empty_cache()
         log("chunked prefill workload, gated RMSNorm epilogue")
@@ -467,7 +487,8 @@ def main():
                           "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel + norm_kernel", "bound": "mfma",
                                        "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                                       "frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                                       "traffic": measured_traffic(NORM_PROFILE, "chunk+norm", "chunked prefill"),
                                        "algorithmic_flops_per_launch": flops,
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls, c
@@ -521,20 +542,26 @@ def main():
                               "tok_per_s": B * S / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": B * S,
                               "roofline": {"kernel": "conv_prefill_kernel" if slots is None else "conv_decode_kernel",
                                            "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                           "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                                           "frac": gbs / HBM_PEAK_GBS,
+                                           "traffic": measured_traffic(CONV_PROFILE, "conv", name),
                                            "algorithmic_bytes_per_launch": bytes_call}})
             del keep, calls
             torch.cuda.empty_cache()
 
+    # Oracle samples: the whole chunked prefill workload (128 units, about
+    # 2.5 s on 16 cores); every 8th unit of the varlen one (128 of 1024,
+    # about 1/8 of its token-heads).
     prefill_sets = []
     if args.only in (None, "prefill"):
         prefill_sets.append(("chunked prefill", 4, "B=4 S=4096 Nk=16 Nv=32 Dk=Dv=128 bf16, g, initial state, C=64",
-                             [(0, 0), (1, 9), (2, 18), (3, 27)], "chunk_kernels_chunked_prefill.txt"))
-    if args.varlen or args.only == "varlen":
+                             [(b, h) for b in range(4) for h in range(32)], True,
+                             "chunk_kernels_chunked_prefill.txt"))
+    if args.only in (None, "varlen"):
         prefill_sets.append(("varlen prefill", 5, "B=16 S=16384 (lengths U{256..16384}) Nk=16 Nv=64 Dk=Dv=128 "
-                             "bf16, no decay, zero initial state, C=64", [(0, 0), (5, 40)],
+                             "bf16, no decay, zero initial state, C=64",
+                             [(b, h) for b in range(16) for h in range(64)][::8], False,
                              "chunk_kernels_varlen_prefill.txt"))
-    for name, cid, desc, units, profile in prefill_sets:
+    for name, cid, desc, units, whole, profile in prefill_sets:
         log(f"{name}: generating inputs")
         c = synth.config(cid)
         bytes_call, flops, tok = prefill_work(c)
@@ -556,7 +583,7 @@ def main():
         torch.cuda.empty_cache()
         if not args.no_cpu:
             log(f"{name}: oracle CPU baseline")
-            entry["cpu_baseline"] = cpu_baseline_prefill(c, units, name)
+            entry["cpu_baseline"] = cpu_baseline_prefill(c, units, name, whole)
         secondary.append(entry)
         del c
 

@@ -1125,14 +1125,20 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
             const int nwg = (units + 8 * G - 1) / (8 * G) * (8 * G);
             int u = units;
             void *args[] = {&pc, &u};
-            // Raise the dynamic-LDS limit once per process (first launch).
-            static std::atomic<int> attr_done{0};
-            if (!attr_done.load(std::memory_order_acquire)) {
+            // Raise the dynamic-LDS limit once per device (its first launch
+            // there). The only state the library keeps: one bit per device,
+            // set after the attribute is in place; racing first calls both
+            // set it, which is harmless.
+            static std::atomic<uint64_t> attr_done{0};
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+            const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+            if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
                 for (const void *f : {(const void *)chunk_mfma_kernel<false>, (const void *)chunk_mfma_kernel<true>}) {
                     hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::LDS_BYTES);
                     if (e != hipSuccess) return e;
                 }
-                attr_done.store(1, std::memory_order_release);
+                attr_done.fetch_or(bit, std::memory_order_acq_rel);
             }
             const void *fn = pc.gate_a ? (const void *)chunk_mfma_kernel<true> : (const void *)chunk_mfma_kernel<false>;
             return hipLaunchKernel(fn, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);

@@ -888,7 +888,10 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
                          bool *norm_done)
 {
     *norm_done = false;
-    if (dtype == 1 && p.S == 1 && Dk == s1::DK && Dv == s1::DV) {
+    // decode_s1_kernel reads beta (and a) of two heads as one 32-bit word, so
+    // it takes an even number of heads; odd counts go to decode_mt_kernel,
+    // whose bounded 16-bit loads never read past the last head.
+    if (dtype == 1 && p.S == 1 && Dk == s1::DK && Dv == s1::DV && ((int64_t)p.B * p.Nv) % 2 == 0) {
         *supported = true;
         *norm_done = true;
         const int nheads = p.B * p.Nv;
@@ -908,7 +911,7 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
         const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
-    if (dtype == 1 && p.S >= 2 && Dk == mt::DK && Dv == mt::DV) {
+    if (dtype == 1 && Dk == mt::DK && Dv == mt::DV) {
         *supported = true;
         *norm_done = true;
         DecodeParams pc = p;

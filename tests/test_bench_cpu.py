@@ -79,6 +79,15 @@ def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch)
     assert bench.measured_traffic("stale.txt", "decode") is None
     assert bench.measured_traffic("nohash.txt", "decode") is None
     assert bench.measured_traffic("missing.txt", "decode") is None
+    # a summary of several launches: one labelled figure each, one hash per source kind
+    multi = prof / "multi.txt"
+    multi.write_text(f"kernel source sha256 [decode]: `{bench.source_hash('decode')}`\n"
+                     f"kernel source sha256 [chunk+norm]: `{'1' * 64}`\n"
+                     "traffic bytes per launch [decode step]: `111`\n"
+                     "traffic bytes per launch [chunked prefill]: `222`\n")
+    assert bench.measured_traffic("multi.txt", "decode", "decode step") == 111
+    assert bench.measured_traffic("multi.txt", "chunk+norm", "chunked prefill") is None   # stale hash
+    assert bench.measured_traffic("multi.txt", "decode", "conv1d prefill") is None         # no such figure
 
 
 def test_more_than_one_gpu_is_refused():

@@ -188,6 +188,17 @@ def test_single_token_one_head():
     _check_decode(c, out, pool)
 
 
+@pytest.mark.parametrize("gk", [None, (-0.5, -0.001)])
+def test_single_token_odd_head_count(gk):
+    # 3 x 3 = 9 heads: an odd number of beta values. The one-token kernel reads
+    # beta of two heads as one 32-bit word, which would run one element past
+    # the tensor here; such calls run the multi-token kernel, which reads each
+    # head's beta alone.
+    c = synth.decode_case(B=3, Nk=1, Nv=3, S=1, Dk=128, Dv=128, slots=5, gk=gk, base=4646)
+    out, pool = run_decode(c)
+    _check_decode(c, out, pool)
+
+
 @pytest.mark.parametrize("S,gk", [(2, (-0.5, -0.001)), (3, None), (4, (-0.3, -0.01))])
 def test_multi_token_many_heads_and_skips(S, gk):
     # 41 * 16 = 656 heads; lengths 0..S+1 (clamped to S), accepted counts
