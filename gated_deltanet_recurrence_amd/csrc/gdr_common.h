@@ -234,6 +234,16 @@ __device__ __forceinline__ int32_t ld_const(const int32_t *p, size_t i)
     return ((cint_ptr)p)[i];
 }
 
+// Cache policy of the decode kernels' state traffic: the state pool is read
+// once and written once per call, in whole 128-byte lines, so both its loads
+// and its stores are non-temporal (the nt bit, the aux argument of the buffer
+// intrinsics) and stream past the caches. Measured on the decode step
+// workload (per call): 30.6 us with neither, 28.8 us with nt loads only,
+// 31.8 us with nt stores only, 26.2 us with both. Stores that cover only part
+// of a line (the prefill's 8-byte output pieces) keep the default policy:
+// non-temporal, they cost the chunked prefill 10 us.
+constexpr int STREAM = 2;
+
 // Wave-uniform value in a scalar register.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

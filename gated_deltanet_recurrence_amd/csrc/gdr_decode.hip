@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         const auto srs = brsrc(pool + ((size_t)(on ? H.r : 0) * Nv + H.h) * DK * DV, on ? DK * DV * 2 : 0);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
-            H.st[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+            H.st[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
         const size_t qk = (size_t)H.b * p.Nk + H.h / rep;
         const int tb = on ? DK * 2 : 0;
         H.k = __builtin_amdgcn_raw_buffer_load_b64(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
             for (int c = 0; c < 8; c += 2)
                 ow[c >> 1] = pack_bf16x2(fmaf(bf16_lo(sw[i][c >> 1]), dd[i], kr[i] * dl[c]),
                                          fmaf(bf16_hi(sw[i][c >> 1]), dd[i], kr[i] * dl[c + 1]));
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, srs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, srs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
         }
     };
 
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
         const auto srs = brsrc(static_cast<const bf16_t *>(p.pool) + ((size_t)r * Nv + h) * DK * DV, DK * DV * 2);
         u32x4_t sw[NI];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) sw[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+        for (int i = 0; i < NI; ++i) sw[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const uint32_t w4[4] = {sw[i].x, sw[i].y, sw[i].z, sw[i].w};
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
                 uint32_t ow[4];
 #pragma unroll
                 for (int c = 0; c < 8; c += 2) ow[c >> 1] = pack_bf16x2(st[i][c], st[i][c + 1]);
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, wrs, ((row0 + i) * DV + cg * 8) * 2, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, wrs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
             }
         }
         cur = nxt;
