@@ -459,9 +459,13 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
+            // A select of values, not of arrays: a runtime choice between x0
+            // and x1 keeps them out of registers (the compiler then places
+            // them in LDS, 32 KB per workgroup, which also halves occupancy).
             const int qa = 4 * (j >> 3) + (j & 3);
-            const float *src = ((j >> 2) & 1) ? x1 : x0;
-            const float gjr = sb ? src[8 + qa] : src[qa];
+            const float lo = ((j >> 2) & 1) ? x1[qa] : x0[qa];
+            const float hi = ((j >> 2) & 1) ? x1[8 + qa] : x0[8 + qa];
+            const float gjr = sb ? hi : lo;
             // Exponent selected before exp2: past the diagonal it could overflow.
             const float ex = __builtin_amdgcn_exp2f(j < r ? grow - gcol[j] : -INFINITY);
             na[j] = -(brow * ex * gjr);
