@@ -33,6 +33,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+F16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix peak
 METRIC = "decode tok/s + state GB/s (%HBM); prefill tok/s + TFLOP/s (%MFMA), Dk=Dv=128"
 
 
@@ -45,7 +46,11 @@ def dev(a):
 
 
 def esize(dtype):
-    return 2 if dtype == "bf16" else 4
+    return 4 if dtype == "f32" else 2
+
+
+def dtype_code(dtype):
+    return {"bf16": gdr.GDR_BF16, "f16": gdr.GDR_F16, "f32": gdr.GDR_F32}[dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -237,7 +242,7 @@ def decode_calls(c, copies, fused=None, norm=None):
         t["out"] = torch.empty((c.B, c.Nv, c.S, c.Dv), dtype=t["q"].dtype, device="cuda")
         t["gates"] = fused_gate_tensors(c, fused)
         p = lambda x: None if x is None else x.data_ptr()
-        a = gdr.DecodeArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S,
+        a = gdr.DecodeArgs(dtype_code(c.dtype), c.B, c.Nk, c.Nv, c.S,
                            c.Dk, c.Dv, c.state.shape[0], c.idx.size, p(t["q"]), p(t["k"]), p(t["v"]),
                            p(t["beta"]), p(t["g"]), p(t["gk"]), p(t["pool"]), p(t["lens"]), p(t["idx"]),
                            p(t["nacc"]), c.scale, p(t["out"]), *[p(x) for x in (t["gates"] or [None] * 4)])
@@ -262,7 +267,7 @@ def chunk_calls(c, copies, fused=None, norm=None):
         t["fin"] = torch.empty((c.B, c.Nv, c.Dk, c.Dv), dtype=t["q"].dtype, device="cuda")
         t["gates"] = fused_gate_tensors(c, fused)
         p = lambda x: None if x is None else x.data_ptr()
-        a = gdr.ChunkArgs(gdr.GDR_BF16 if c.dtype == "bf16" else gdr.GDR_F32, c.B, c.Nk, c.Nv, c.S, c.Dk,
+        a = gdr.ChunkArgs(dtype_code(c.dtype), c.B, c.Nk, c.Nv, c.S, c.Dk,
                           c.Dv, c.chunk, p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["g"]),
                           p(t["init"]), p(t["lens"]), c.scale, p(t["out"]), p(t["fin"]), None, 0,
                           *[p(x) for x in (t["gates"] or [None] * 4)])
@@ -345,7 +350,7 @@ def main():
     ap.add_argument("--launch", choices=["graph", "eager"], default="graph")
     ap.add_argument("--copies", type=int, default=8, help="decode pool copies rotated per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused", "norm", "conv"], default=None)
+    ap.add_argument("--only", choices=["decode", "spec", "prefill", "varlen", "fused", "norm", "conv", "f16"], default=None)
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
@@ -450,6 +455,42 @@ def main():
                                        "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                        "frac": tf / BF16_MFMA_PEAK_TFLOPS,
                                        "traffic": measured_traffic(FUSED_PROFILE, "chunk", "chunked prefill"),
+                                       "algorithmic_flops_per_launch": flops,
+                                       "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls, c
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "f16"):
+        # The decode step and chunked prefill workloads with fp16 I/O (the
+        # prefill operator's other accepted dtype): same shapes, distributions
+        # and seeds, stored in IEEE half.
+        log("decode step workload, fp16")
+        c = synth.config(2, dtype="f16")
+        state_b, bytes_call, tok = decode_bytes(c)
+        calls, keep = decode_calls(c, args.copies)
+        ms, wall, _ = time_calls(calls, args.steps, args.warmup, use_graph)
+        gbs = bytes_call / (ms * 1e-3) / 1e9
+        secondary.append({"workload": "decode step, fp16: B=64 Nk=16 Nv=32 S=1 Dk=Dv=128 fp16, 64-slot fp16 pool",
+                          "dtype": "f16", "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "state_GBps": state_b / (ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "decode_s1_kernel (fp16)", "bound": "hbm", "achieved": gbs,
+                                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                       "traffic": None, "algorithmic_bytes_per_launch": bytes_call}})
+        del keep, calls
+        torch.cuda.empty_cache()
+        log("chunked prefill workload, fp16")
+        c = synth.config(4, dtype="f16")
+        bytes_call, flops, tok = prefill_work(c)
+        calls, keep = chunk_calls(c, 2)
+        ms, wall, _ = time_calls(calls, max(10, args.steps // 8), max(2, args.warmup // 8), use_graph)
+        tf = flops / (ms * 1e-3) / 1e12
+        secondary.append({"workload": "chunked prefill, fp16: B=4 S=4096 Nk=16 Nv=32 Dk=Dv=128 fp16, g, initial "
+                                      "state, C=64", "dtype": "f16",
+                          "tok_per_s": tok / (ms * 1e-3), "ms_per_call": ms, "tokens_per_call": tok,
+                          "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
+                          "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel (fp16)", "bound": "mfma",
+                                       "achieved": tf, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": tf / F16_MFMA_PEAK_TFLOPS, "traffic": None,
                                        "algorithmic_flops_per_launch": flops,
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls, c

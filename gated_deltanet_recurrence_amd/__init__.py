@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_OK, GDR_ERR_NULL, GDR_ERR_SHAPE, GDR_ERR_DTYPE, GDR_ERR_UNSUPPORTED, GDR_ERR_LAUNCH, GDR_ERR_SCRATCH_LIMIT = range(7)
 GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
-GDR_F32, GDR_BF16 = 0, 1
+GDR_F32, GDR_BF16, GDR_F16 = 0, 1, 2
 
 _vp = ctypes.c_void_p
 
@@ -119,7 +119,7 @@ def _check(rc: int, what: str):
     raise RuntimeError(msg)
 
 
-_DT = {torch.bfloat16: GDR_BF16, torch.float32: GDR_F32}
+_DT = {torch.bfloat16: GDR_BF16, torch.float16: GDR_F16, torch.float32: GDR_F32}
 
 
 def _ptr(t):

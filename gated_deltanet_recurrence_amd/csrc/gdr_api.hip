@@ -80,7 +80,7 @@ hipError_t launch_norm_pass(const Args *a, void *stream, bool *ok)
 template <typename Args>
 gdr_status check_conv(const Args *a, int max_S)
 {
-    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16 && a->dtype != GDR_F16) return GDR_ERR_DTYPE;
     if (a->B < 0 || a->S < 1 || a->S > max_S || a->Nk < 1 || a->Nv < 1 || a->Dk < 1 || a->Dv < 1 ||
         a->Nv % a->Nk != 0 || a->Dk % 2 != 0 || a->Dv % 2 != 0 || a->K < 1 || a->K > 8)
         return GDR_ERR_SHAPE;
@@ -131,7 +131,7 @@ const char *gdr_status_string(gdr_status s)
 gdr_status gdr_decode(const gdr_decode_args *a, void *stream)
 {
     if (!a) return GDR_ERR_NULL;
-    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16 && a->dtype != GDR_F16) return GDR_ERR_DTYPE;
     if (a->B < 0 || a->S < 1 || a->S > 8 || a->Nk < 1 || a->Nv < 1 || a->Dk < 1 || a->Dv < 1 ||
         a->num_slots < 1 || a->Nv % a->Nk != 0)
         return GDR_ERR_SHAPE;
@@ -187,7 +187,7 @@ namespace {
 gdr_status chunk_call(const gdr_chunk_args *a, void *stream, bool noalloc)
 {
     if (!a) return GDR_ERR_NULL;
-    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16) return GDR_ERR_DTYPE;
+    if (a->dtype != GDR_F32 && a->dtype != GDR_BF16 && a->dtype != GDR_F16) return GDR_ERR_DTYPE;
     if (a->B < 0 || a->S < 0 || a->Nk < 1 || a->Nv < 1 || a->Dk < 1 || a->Dv < 1 ||
         a->chunk_size < 1 || a->Nv % a->Nk != 0)
         return GDR_ERR_SHAPE;

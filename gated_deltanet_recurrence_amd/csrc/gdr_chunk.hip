@@ -20,13 +20,14 @@
 // so padded inputs are never read; their outputs are written as exact zeros.
 //
 // Kernels:
-//  * chunk_t_kernel + chunk_mfma_kernel — bf16 I/O, Dk = Dv = 128, C = 64.
+//  * chunk_t_kernel + chunk_mfma_kernel — bf16 or fp16 I/O, Dk = Dv = 128, C = 64.
 //    chunk_t_kernel forms T = (I + A)^-1 of every chunk of every sequence in
 //    parallel (it depends on k, beta and g only) into the caller's workspace;
 //    chunk_mfma_kernel then makes one pass over the chunks per (sequence,
 //    value head, 64-column tile of Dv), carrying its slice of the state in
 //    float32 matrix-core accumulators. All dense products run on
-//    v_mfma_f32_32x32x16_bf16 with bf16 operands.
+//    v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x16_f16 for fp16 I/O) with
+//    operands in the I/O format.
 //  * chunk_f32_kernel — float32 I/O, small heads. The same chunk algorithm in
 //    plain float32 arithmetic; T by row-wise forward substitution.
 #include <atomic>
@@ -36,8 +37,10 @@
 
 namespace gdr {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+// Eight 16-bit elements, the operand of one MFMA k-step: bf16, or fp16 bit
+// patterns (reinterpreted where the fp16 MFMA takes them).
+typedef __bf16 e16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -50,9 +53,15 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // left operand and column l % 32 of the right one, each as 8 consecutive
 // k-values starting at 8h; the result gives lane l column l % 32, register q
 // holding row 8(q / 4) + 4h + q % 4.
-__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c)
+// v_mfma_f32_32x32x16_f16 has the same shape and lane layout.
+template <typename EL> __device__ __forceinline__ f32x16_t mfma32(e16x8_t a, e16x8_t b, f32x16_t c);
+template <> __device__ __forceinline__ f32x16_t mfma32<BF16>(e16x8_t a, e16x8_t b, f32x16_t c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16_t mfma32<F16>(e16x8_t a, e16x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16_t zero16()
 {
@@ -71,18 +80,26 @@ __device__ __forceinline__ int drow(int q, int hh) { return 8 * (q >> 2) + 4 * h
 // 4h + e % 4 + 8(e / 4), i.e. bits 2 and 3 of the index are swapped ("k-order").
 // Every operand tile in LDS is kept in k-order along its contraction axis, so
 // each lane reads or writes one 16-byte piece per k-step.
-__device__ __forceinline__ bf16x8_t op8(const f32x16_t &d, int s)
+template <typename EL>
+__device__ __forceinline__ e16x8_t op8(const f32x16_t &d, int s)
 {
-    bf16x8_t r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)d[8 * s + e];
-    return r;
+    const u32x4_t w = {EL::pack(d[8 * s], d[8 * s + 1]), EL::pack(d[8 * s + 2], d[8 * s + 3]),
+                       EL::pack(d[8 * s + 4], d[8 * s + 5]), EL::pack(d[8 * s + 6], d[8 * s + 7])};
+    return __builtin_bit_cast(e16x8_t, w);
+}
+// Eight floats narrowed into one operand.
+template <typename EL>
+__device__ __forceinline__ e16x8_t pack8(const float (&x)[8])
+{
+    const u32x4_t w = {EL::pack(x[0], x[1]), EL::pack(x[2], x[3]), EL::pack(x[4], x[5]), EL::pack(x[6], x[7])};
+    return __builtin_bit_cast(e16x8_t, w);
 }
 // D(X Y) + c over a 32-long contraction, from D(X^T) and D(Y).
+template <typename EL>
 __device__ __forceinline__ f32x16_t prod(const f32x16_t &dxt, const f32x16_t &dy, f32x16_t c)
 {
-    c = mfma32(op8(dxt, 0), op8(dy, 0), c);
-    return mfma32(op8(dxt, 1), op8(dy, 1), c);
+    c = mfma32<EL>(op8<EL>(dxt, 0), op8<EL>(dy, 0), c);
+    return mfma32<EL>(op8<EL>(dxt, 1), op8<EL>(dy, 1), c);
 }
 
 // Byte offset of 16-byte piece u of row r in a tile of 256- or 128-byte rows.
@@ -97,13 +114,13 @@ __device__ __forceinline__ int sw128(int r, int u) { return (r << 7) + ((u ^ ((r
 __device__ __forceinline__ int sw256t(int r, int u) { return (r << 8) + ((u ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 4); }
 __device__ __forceinline__ int sw128t(int r, int u) { return (r << 7) + ((u ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))) << 4); }
 
-__device__ __forceinline__ bf16x8_t ld8(const unsigned char *base, int off)
+__device__ __forceinline__ e16x8_t ld8(const unsigned char *base, int off)
 {
-    return *reinterpret_cast<const bf16x8_t *>(base + off);
+    return *reinterpret_cast<const e16x8_t *>(base + off);
 }
-__device__ __forceinline__ void st8(unsigned char *base, int off, bf16x8_t v)
+__device__ __forceinline__ void st8(unsigned char *base, int off, e16x8_t v)
 {
-    *reinterpret_cast<bf16x8_t *>(base + off) = v;
+    *reinterpret_cast<e16x8_t *>(base + off) = v;
 }
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -119,7 +136,7 @@ typedef __attribute__((address_space(3))) i16x4_t *lds_i16x4_ptr;
 // i % 4 of the 4 elements named by source lanes 4j + i / 4 (j = 0..3), so
 // source lane m names row T(m / 4) and columns c + 4(m % 4) .. + 3.
 template <int PITCH>
-__device__ __forceinline__ bf16x8_t ldT(const unsigned char *base, int cb, int ks, int lane)
+__device__ __forceinline__ e16x8_t ldT(const unsigned char *base, int cb, int ks, int lane)
 {
     const int g = lane >> 4, m = lane & 15;
     const int row = 16 * ks + 4 * (g >> 1) + (m >> 2);
@@ -130,7 +147,7 @@ __device__ __forceinline__ bf16x8_t ldT(const unsigned char *base, int cb, int k
     const int o2 = (PITCH == 256 ? sw256t(row + 8, piece) : sw128t(row + 8, piece)) + half;
     const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + o1));
     const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(base + o2));
-    return __builtin_bit_cast(bf16x8_t, i16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
+    return __builtin_bit_cast(e16x8_t, i16x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]});
 }
 
 // Left operand n (0-5) of a product with T diag(fac), from a chunk's T kept as
@@ -144,7 +161,9 @@ __device__ __forceinline__ int t_operand_offset(int n, int lane)
     const int j = n < 2 ? 0 : (n < 4 ? 2 : 1), s = n & 1;
     return ((2 * j + s) * 64 + lane) * 16;
 }
-__device__ __forceinline__ bf16x8_t t_operand(const unsigned char *tbase, int n, const float *fac, int lane)
+// NEG: the operand of -T diag(fac), the sign taken by the multiply.
+template <typename EL, bool NEG = false>
+__device__ __forceinline__ e16x8_t t_operand(const unsigned char *tbase, int n, const float *fac, int lane)
 {
     const int k2 = n < 2 ? n : n - 2;
     const u32x4_t t4 = *reinterpret_cast<const u32x4_t *>(tbase + t_operand_offset(n, lane));
@@ -152,10 +171,10 @@ __device__ __forceinline__ bf16x8_t t_operand(const unsigned char *tbase, int n,
     const float4 f0 = *reinterpret_cast<const float4 *>(fac + i0), f1 = *reinterpret_cast<const float4 *>(fac + i0 + 8);
     const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
     const uint32_t w4[4] = {t4.x, t4.y, t4.z, t4.w};
-    bf16x8_t r;
+    float r[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(((e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1])) * fe[e]);
-    return r;
+    for (int e = 0; e < 8; ++e) r[e] = ((e & 1) ? EL::hi(w4[e >> 1]) : EL::lo(w4[e >> 1])) * (NEG ? -fe[e] : fe[e]);
+    return pack8<EL>(r);
 }
 
 namespace mk {
@@ -222,7 +241,7 @@ __device__ __forceinline__ float row_lanes_sum(float x)
     if constexpr (LANES == 16) x += dpp_f<0x140, 0xf>(x);   // row_mirror: the other half
     return x;
 }
-template <int LANES, int W>
+template <typename EL, int LANES, int W>
 __device__ __forceinline__ void normalise_row(u32x4_t (&x)[W])
 {
     float ss = 0.f;
@@ -231,8 +250,8 @@ __device__ __forceinline__ void normalise_row(u32x4_t (&x)[W])
         const uint32_t a[4] = {x[w].x, x[w].y, x[w].z, x[w].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            ss = fmaf(bf16_lo(a[e]), bf16_lo(a[e]), ss);
-            ss = fmaf(bf16_hi(a[e]), bf16_hi(a[e]), ss);
+            ss = fmaf(EL::lo(a[e]), EL::lo(a[e]), ss);
+            ss = fmaf(EL::hi(a[e]), EL::hi(a[e]), ss);
         }
     }
     const float r = qk_rnorm(row_lanes_sum<LANES>(ss));
@@ -241,7 +260,7 @@ __device__ __forceinline__ void normalise_row(u32x4_t (&x)[W])
         const uint32_t a[4] = {x[w].x, x[w].y, x[w].z, x[w].w};
         uint32_t o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(bf16_lo(a[e]) * r, bf16_hi(a[e]) * r);
+        for (int e = 0; e < 4; ++e) o[e] = EL::pack(EL::lo(a[e]) * r, EL::hi(a[e]) * r);
         x[w] = u32x4_t{o[0], o[1], o[2], o[3]};
     }
 }
@@ -315,6 +334,7 @@ __device__ __forceinline__ void fsub16(float (&x)[16], const float (&na)[16])
     }
 }
 
+template <typename EL>
 __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(3, 3))) void chunk_t_kernel(ChunkParams p, int nchk, int units)
 {
     using namespace mk;
@@ -347,7 +367,7 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     // The chunk's 16 KB are read as 16 whole-row loads (1 KB, 4 rows each) and
     // turned into operands through this wave's LDS half tile, one half at a
     // time (a wave's LDS accesses complete in order, so no barrier is needed).
-    const bf16_t *kb = static_cast<const bf16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
+    const uint16_t *kb = static_cast<const uint16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, L * DK * 2, 0x00020000);
     u32x4_t kr[16];
 #pragma unroll
@@ -357,11 +377,11 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             u32x4_t one[1] = {kr[i]};
-            normalise_row<16>(one);
+            normalise_row<EL, 16>(one);
             kr[i] = one[0];
         }
     }
-    bf16x8_t kf[2][8];
+    e16x8_t kf[2][8];
     unsigned char *kt = kst[wl];
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
@@ -375,21 +395,21 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     {
         const size_t vh = (size_t)b * Nv + h;
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(static_cast<const bf16_t *>(p.beta) + vh * S), (short)0, L * 2, 0x00020000);
-        // g, or with fused gates the raw input a (bf16).
+            (void *)(static_cast<const uint16_t *>(p.beta) + vh * S), (short)0, L * 2, 0x00020000);
+        // g, or with fused gates the raw input a (16-bit).
         const bool fg = p.gate_a != nullptr;
         const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
-            fg ? (void *)(static_cast<const bf16_t *>(p.gate_a) + vh * S) : (void *)(p.g ? p.g + vh * S : nullptr),
+            fg ? (void *)(static_cast<const uint16_t *>(p.gate_a) + vh * S) : (void *)(p.g ? p.g + vh * S : nullptr),
             (short)0, fg ? L * 2 : (p.g ? L * 4 : 0), 0x00020000);
         const uint32_t rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
         const uint32_t rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
                                : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
-        float beta = __uint_as_float(rb << 16), g = __uint_as_float(rg);
+        float beta = EL::to(rb), g = __uint_as_float(rg);
         if (fg) {
             // Tokens past the length are identity steps: beta = g = 0.
             const bool valid = t0 + lane < L;
             beta = valid ? gate_sigmoid(beta) : 0.f;
-            g = valid ? gate_g(__uint_as_float(rg << 16), p.A_log[h], p.dt_bias[h]) : 0.f;
+            g = valid ? gate_g(EL::to(rg), p.A_log[h], p.dt_bias[h]) : 0.f;
         }
         bgs[wl][lane] = beta;
         bgs[wl][64 + lane] = wave_prefix_sum(g) * 1.44269504088896340736f;
@@ -409,15 +429,15 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     f32x16_t G0 = zero16(), G1 = zero16(), G10 = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        G0 = mfma32(kf[0][ks], kf[0][ks], G0);
-        G1 = mfma32(kf[1][ks], kf[1][ks], G1);
-        G10 = mfma32(kf[1][ks], kf[0][ks], G10);
+        G0 = mfma32<EL>(kf[0][ks], kf[0][ks], G0);
+        G1 = mfma32<EL>(kf[1][ks], kf[1][ks], G1);
+        G10 = mfma32<EL>(kf[1][ks], kf[0][ks], G10);
     }
 
     // Off-diagonal 16x16 block of each 32-block d (its rows 16-31 against
     // columns 0-15) as the left operand of k-step 1: registers 8-15 of D(A_dd)
     // in the lanes of columns 0-15, zero elsewhere.
-    bf16x8_t aoff[2];
+    e16x8_t aoff[2];
     {
         float br[16], gr[16];
 #pragma unroll
@@ -428,9 +448,11 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
             const f32x16_t &G = d ? G1 : G0;
             // -inf as the exponent, not a select of the product: the select
             // compiles to one branch per element, each with its own wait.
+            float a8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                aoff[d][e] = (__bf16)(br[8 + e] * __builtin_amdgcn_exp2f(c32 < 16 ? gr[8 + e] - gc : -INFINITY) * G[8 + e]);
+                a8[e] = br[8 + e] * __builtin_amdgcn_exp2f(c32 < 16 ? gr[8 + e] - gc : -INFINITY) * G[8 + e];
+            aoff[d] = pack8<EL>(a8);
         }
     }
 
@@ -487,20 +509,22 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
         R0[q] = __uint_as_float(s[0]);
         R1[q] = __uint_as_float(s[1]);
     }
-    bf16x8_t eye[2];
+    e16x8_t eye[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 2; ++s) {
+        float one[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            eye[s][e] = (__bf16)((16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f);
+        for (int e = 0; e < 8; ++e) one[e] = (16 * s + 4 * hh + (e & 3) + 8 * (e >> 2)) == c32 ? 1.f : 0.f;
+        eye[s] = pack8<EL>(one);
+    }
     // Merge inside each 32-block: T_dd^T = D_dd^T - D_dd^T Aoff^T D_dd^T.
     // Y = Aoff^T D_dd^T has nonzero rows 0-15 only (k-step 0 of the next
     // product), Aoff nonzero rows 16-31 only (k-step 1 of this one); the left
     // factor D_dd (not transposed) comes from D_dd^T and the identity.
-    auto merge16 = [&](f32x16_t &R, const bf16x8_t &ao) __attribute__((always_inline)) {
-        const f32x16_t Y = mfma32(ao, op8(R, 1), zero16());
-        const f32x16_t E = -mfma32(op8(R, 0), eye[0], zero16());
-        R = mfma32(op8(E, 0), op8(Y, 0), R);
+    auto merge16 = [&](f32x16_t &R, const e16x8_t &ao) __attribute__((always_inline)) {
+        const f32x16_t Y = mfma32<EL>(ao, op8<EL>(R, 1), zero16());
+        const f32x16_t E = -mfma32<EL>(op8<EL>(R, 0), eye[0], zero16());
+        R = mfma32<EL>(op8<EL>(E, 0), op8<EL>(Y, 0), R);
     };
     merge16(R0, aoff[0]);
     merge16(R1, aoff[1]);
@@ -516,21 +540,21 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     }
     unsigned char *tw = static_cast<unsigned char *>(p.work) + (((size_t)b * Nv + h) * nchk + c) * tk::CHUNK_ELEMS * 2;
     // k-step s of block j, in register order.
-    auto put = [&](int j, int s, bf16x8_t v) __attribute__((always_inline)) {
-        *reinterpret_cast<bf16x8_t *>(tw + ((2 * j + s) * 64 + lane) * 16) = v;
+    auto put = [&](int j, int s, e16x8_t v) __attribute__((always_inline)) {
+        *reinterpret_cast<e16x8_t *>(tw + ((2 * j + s) * 64 + lane) * 16) = v;
     };
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-        put(0, s, op8(R0, s));
-        put(1, s, op8(R1, s));
+        put(0, s, op8<EL>(R0, s));
+        put(1, s, op8<EL>(R1, s));
     }
     // T_10^T = -T_00^T A_10^T T_11^T, with D(T_00) from D(T_00^T) and the identity.
-    const f32x16_t Z = -prod(G10, R1, zero16());
-    f32x16_t T0 = mfma32(op8(R0, 0), eye[0], zero16());
-    T0 = mfma32(op8(R0, 1), eye[1], T0);
-    const f32x16_t T10 = prod(T0, Z, zero16());
+    const f32x16_t Z = -prod<EL>(G10, R1, zero16());
+    f32x16_t T0 = mfma32<EL>(op8<EL>(R0, 0), eye[0], zero16());
+    T0 = mfma32<EL>(op8<EL>(R0, 1), eye[1], T0);
+    const f32x16_t T10 = prod<EL>(T0, Z, zero16());
 #pragma unroll
-    for (int s = 0; s < 2; ++s) put(2, s, op8(T10, s));
+    for (int s = 0; s < 2; ++s) put(2, s, op8<EL>(T10, s));
 }
 
 // One workgroup per (sequence, value head, 64-column tile of Dv); the columns
@@ -558,7 +582,7 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 // reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
 // FG: fused gates (raw a and beta logits in place of g and beta).
-template <bool FG>
+template <typename EL, bool FG>
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
     using namespace mk;
@@ -595,20 +619,20 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     L = L < 0 ? 0 : (L > S ? S : L);
     const int nchunks = (L + C - 1) / C;
 
-    const bf16_t *qb = static_cast<const bf16_t *>(p.q) + ((size_t)b * Nk + kh) * S * DK;
-    const bf16_t *kb = static_cast<const bf16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
-    const bf16_t *vb = static_cast<const bf16_t *>(p.v) + ((size_t)b * Nv + h) * S * DV + col0;
-    const bf16_t *betab = static_cast<const bf16_t *>(p.beta) + ((size_t)b * Nv + h) * S;
-    // g (float32), or with fused gates the raw input a (bf16)
+    const uint16_t *qb = static_cast<const uint16_t *>(p.q) + ((size_t)b * Nk + kh) * S * DK;
+    const uint16_t *kb = static_cast<const uint16_t *>(p.k) + ((size_t)b * Nk + kh) * S * DK;
+    const uint16_t *vb = static_cast<const uint16_t *>(p.v) + ((size_t)b * Nv + h) * S * DV + col0;
+    const uint16_t *betab = static_cast<const uint16_t *>(p.beta) + ((size_t)b * Nv + h) * S;
+    // g (float32), or with fused gates the raw input a (16-bit)
     constexpr bool fg = FG;
-    const void *gb = fg ? (const void *)(static_cast<const bf16_t *>(p.gate_a) + ((size_t)b * Nv + h) * S)
+    const void *gb = fg ? (const void *)(static_cast<const uint16_t *>(p.gate_a) + ((size_t)b * Nv + h) * S)
                         : (const void *)(p.g ? p.g + ((size_t)b * Nv + h) * S : nullptr);
     // The fused gates' per-head parameters, read once: inside the chunk loop
     // the stores to the outputs keep the compiler from hoisting them.
     const float a_log = fg ? p.A_log[h] : 0.f, dt_b = fg ? p.dt_bias[h] : 0.f;
-    bf16_t *ob = static_cast<bf16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV + col0;
-    const bf16_t *ib = p.init ? static_cast<const bf16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
-    bf16_t *fb = static_cast<bf16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
+    uint16_t *ob = static_cast<uint16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV + col0;
+    const uint16_t *ib = p.init ? static_cast<const uint16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
+    uint16_t *fb = static_cast<uint16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
 
     uint32_t *flags = reinterpret_cast<uint32_t *>(smem + P_FLAG);
     if (tid < 4) flags[tid] = 0u;
@@ -635,25 +659,24 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             for (int f = 0; f < 4; ++f)
 #pragma unroll
                 for (int q = 0; q < 16; ++q)
-                    st[f][q] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-                                                   irs, ((32 * f + drow(q, hh)) * DV + 32 * cw + c32) * 2, 0, 0)
-                                               << 16);
+                    st[f][q] = EL::to((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+                        irs, ((32 * f + drow(q, hh)) * DV + 32 * cw + c32) * 2, 0, 0));
         }
         if (nchunks > 0) lds_barrier();   // operand set of chunk 0 is ready
         for (int c = 0; c < nchunks; ++c) {
             const unsigned char *set = smem + (c & 1) * SET_BYTES;
             const int t0 = c * C;
 
-            bf16x8_t sop[8];
+            e16x8_t sop[8];
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) sop[ks] = op8(st[ks >> 1], ks & 1);
+            for (int ks = 0; ks < 8; ++ks) sop[ks] = op8<EL>(st[ks >> 1], ks & 1);
 
             // U = T diag(beta) V for this wave's columns (it does not depend on
             // the state), then Vnew = U - W S0 and S0^T Q^T, one pass over the
             // 128 features.
             f32x16_t vn[2], ot[2], uu[2];
             {
-                bf16x8_t bv[4];
+                e16x8_t bv[4];
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<128>(set + S_VT, cw, k2, lane);
 #pragma unroll
@@ -663,12 +686,12 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     uu[rb] = zero16();
 #pragma unroll
                     for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        uu[rb] = mfma32(ld8(set + S_TB, t_operand_offset(rb == 0 ? k2 : 2 + k2, lane)), bv[k2], uu[rb]);
+                        uu[rb] = mfma32<EL>(ld8(set + S_TB, t_operand_offset(rb == 0 ? k2 : 2 + k2, lane)), bv[k2], uu[rb]);
                 }
             }
             {
-                bf16x8_t opd[2][4];
-                auto ldk = [&](int ks, bf16x8_t *o) __attribute__((always_inline)) {
+                e16x8_t opd[2][4];
+                auto ldk = [&](int ks, e16x8_t *o) __attribute__((always_inline)) {
                     o[0] = ld8(set, S_W + sw256(c32, 2 * ks + hh));
                     o[1] = ld8(set, S_W + sw256(32 + c32, 2 * ks + hh));
                     o[2] = ld8(set, S_Q + sw256(c32, 2 * ks + hh));
@@ -679,11 +702,11 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 for (int ks = 0; ks < 8; ++ks) {
                     if (ks + 1 < 8) ldk(ks + 1, opd[(ks + 1) & 1]);
                     __builtin_amdgcn_sched_barrier(0);
-                    const bf16x8_t *o = opd[ks & 1];
-                    vn[0] = mfma32(o[0], sop[ks], vn[0]);
-                    vn[1] = mfma32(o[1], sop[ks], vn[1]);
-                    ot[0] = mfma32(sop[ks], o[2], ot[0]);
-                    ot[1] = mfma32(sop[ks], o[3], ot[1]);
+                    const e16x8_t *o = opd[ks & 1];
+                    vn[0] = mfma32<EL>(o[0], sop[ks], vn[0]);
+                    vn[1] = mfma32<EL>(o[1], sop[ks], vn[1]);
+                    ot[0] = mfma32<EL>(sop[ks], o[2], ot[0]);
+                    ot[1] = mfma32<EL>(sop[ks], o[3], ot[1]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -695,7 +718,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
 
             // Vnew as the left operand of Vnew^T, and decayed as the right
             // operand of the state update.
-            bf16x8_t vna[4], vnb[4];
+            e16x8_t vna[4], vnb[4];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
                 f32x16_t dv;
@@ -709,8 +732,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    vna[2 * rb + s] = op8(vn[rb], s);
-                    vnb[2 * rb + s] = op8(dv, s);
+                    vna[2 * rb + s] = op8<EL>(vn[rb], s);
+                    vnb[2 * rb + s] = op8<EL>(dv, s);
                 }
             }
             // O^T += Vnew^T P^T (P is lower triangular by 32-blocks).
@@ -718,17 +741,15 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                 for (int k2 = 0; k2 < 2 * tb + 2; ++k2)
-                    ot[tb] = mfma32(vna[k2], ld8(set, S_P + sw128(32 * tb + c32, 2 * k2 + hh)), ot[tb]);
+                    ot[tb] = mfma32<EL>(vna[k2], ld8(set, S_P + sw128(32 * tb + c32, 2 * k2 + hh)), ot[tb]);
             // Outputs: lane holds 4 consecutive columns of one token per group.
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) {
                 const int r = 32 * tb + c32;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    bf16x4_t o;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = (__bf16)ot[tb][4 * m + i];
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, o), orsrc,
+                    const u32x2_t o = {EL::pack(ot[tb][4 * m], ot[tb][4 * m + 1]), EL::pack(ot[tb][4 * m + 2], ot[tb][4 * m + 3])};
+                    __builtin_amdgcn_raw_buffer_store_b64(o, orsrc,
                                                           ((t0 + r) * DV + 32 * cw + 8 * m + 4 * hh) * 2, 0, 0);
                 }
             }
@@ -740,14 +761,14 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             for (int f = 0; f < 4; ++f)
 #pragma unroll
                 for (int k2 = 0; k2 < 4; ++k2)
-                    st[f] = mfma32(ldT<256>(set + S_KT, f, k2, lane), vnb[k2], st[f]);
+                    st[f] = mfma32<EL>(ldT<256>(set + S_KT, f, k2, lane), vnb[k2], st[f]);
             lds_barrier();
         }
 #pragma unroll
         for (int f = 0; f < 4; ++f)
 #pragma unroll
             for (int q = 0; q < 16; ++q)
-                fb[(size_t)(32 * f + drow(q, hh)) * DV + 32 * cw + c32] = from_f32<bf16_t>(st[f][q]);
+                fb[(size_t)(32 * f + drow(q, hh)) * DV + 32 * cw + c32] = EL::from(st[f][q]);
     } else {
         // ------------------------------- prep ------------------------------
 
@@ -767,7 +788,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         // chunks that exist; a chunk's 6 KB are copied as they are into its
         // operand set.
         const int nchk = (S + C - 1) / C;
-        const bf16_t *twb = static_cast<const bf16_t *>(p.work) + ((size_t)b * Nv + h) * nchk * tk::CHUNK_ELEMS;
+        const uint16_t *twb = static_cast<const uint16_t *>(p.work) + ((size_t)b * Nv + h) * nchk * tk::CHUNK_ELEMS;
         const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void *)twb, (short)0, nchunks * tk::CHUNK_ELEMS * 2, 0x00020000);
         // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
         // waves 0-1 2 x 32 bytes of V and 3 x 16 bytes of T, wave 1 one beta
@@ -821,8 +842,8 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     if (p.qk_norm) {
                         // A row of K or Q spans 8 consecutive lanes, 32 bytes each.
                         u32x4_t kx[2] = {ra[2 * m], ra[2 * m + 1]}, qx[2] = {ra[4 + 2 * m], ra[5 + 2 * m]};
-                        normalise_row<8>(kx);
-                        normalise_row<8>(qx);
+                        normalise_row<EL, 8>(kx);
+                        normalise_row<EL, 8>(qx);
                         ra[2 * m] = kx[0]; ra[2 * m + 1] = kx[1];
                         ra[4 + 2 * m] = qx[0]; ra[5 + 2 * m] = qx[1];
                     }
@@ -847,11 +868,11 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     // Per-token factors of chunk cn (lane t = token t): gamma is the
                     // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
                     const int nv = min(C, L - cn * C);
-                    float beta = __uint_as_float(rb << 16), g = __uint_as_float(rg);
+                    float beta = EL::to(rb), g = __uint_as_float(rg);
                     if (fg) {
                         // Fused gates; tokens past the length are identity steps.
                         beta = lane < nv ? gate_sigmoid(beta) : 0.f;
-                        g = lane < nv ? gate_g(__uint_as_float(rg << 16), a_log, dt_b) : 0.f;
+                        g = lane < nv ? gate_g(EL::to(rg), a_log, dt_b) : 0.f;
                     }
                     const float gam2 = wave_prefix_sum(g) * 1.44269504088896340736f;
                     const float gamC2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam2), 63));
@@ -886,7 +907,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 f32x16_t G = zero16();
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks)
-                    G = mfma32(ld8(set, S_KT + sw256t(32 * ibq + c32, 2 * ks + hh)),
+                    G = mfma32<EL>(ld8(set, S_KT + sw256t(32 * ibq + c32, 2 * ks + hh)),
                                ld8(set, S_Q + sw256(32 * rbq + c32, 2 * ks + hh)), G);
                 const int r = 32 * rbq + c32;
                 const float gq = gv[r];
@@ -898,7 +919,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     G[q] = i <= r ? p.scale * __builtin_amdgcn_exp2f(gq - gi[q]) * G[q] : 0.f;
                 }
 #pragma unroll
-                for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8(G, s));
+                for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8<EL>(G, s));
             }
             if constexpr (W < 2) {
                 // T diag(beta) for the chain's U, from this lane's three pieces
@@ -910,31 +931,30 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     const float4 f0 = *reinterpret_cast<const float4 *>(bg + i0), f1 = *reinterpret_cast<const float4 *>(bg + i0 + 8);
                     const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
                     const uint32_t w4[4] = {traw[n].x, traw[n].y, traw[n].z, traw[n].w};
-                    bf16x8_t r;
+                    float r[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) r[e] = (__bf16)(((e & 1) ? bf16_hi(w4[e >> 1]) : bf16_lo(w4[e >> 1])) * fe[e]);
-                    st8(set, S_TB + (ltid + 128 * n) * 16, r);
+                    for (int e = 0; e < 8; ++e) r[e] = ((e & 1) ? EL::hi(w4[e >> 1]) : EL::lo(w4[e >> 1])) * fe[e];
+                    st8(set, S_TB + (ltid + 128 * n) * 16, pack8<EL>(r));
                 }
             }
             if constexpr (W == 2 || W == 3 || W == 5) {
                 // -W^T = -(K^T T'^T), T' = T diag(beta exp(gamma)), by 32
                 // features, written as -W rows: feature blocks 2 and 3 on waves
                 // 2 and 3, blocks 0 and 1 on wave 5.
-                bf16x8_t tp[6];
+                e16x8_t tp[6];
 #pragma unroll
-                for (int n = 0; n < 6; ++n) tp[n] = t_operand(set + S_T, n, fv, lane);
+                for (int n = 0; n < 6; ++n) tp[n] = t_operand<EL, true>(set + S_T, n, fv, lane);
                 auto wblock = [&](int fbk) __attribute__((always_inline)) {
-                    bf16x8_t ak[4];
+                    e16x8_t ak[4];
 #pragma unroll
                     for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ldT<256>(set + S_KT, fbk, k2, lane);
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
                         f32x16_t d = zero16();
 #pragma unroll
-                        for (int k2 = 0; k2 < 2 * rb + 2; ++k2) d = mfma32(ak[k2], tp[rb == 0 ? k2 : 2 + k2], d);
-                        d = -d;
+                        for (int k2 = 0; k2 < 2 * rb + 2; ++k2) d = mfma32<EL>(ak[k2], tp[rb == 0 ? k2 : 2 + k2], d);
 #pragma unroll
-                        for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8(d, s));
+                        for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8<EL>(d, s));
                     }
                 };
                 if constexpr (W == 5) {
@@ -1103,7 +1123,7 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkParams p)
 
 int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, int S)
 {
-    if (dtype == 1 && Dk == mk::DK && Dv == mk::DV && C == mk::C)
+    if ((dtype == 1 || dtype == 2) && Dk == mk::DK && Dv == mk::DV && C == mk::C)
         return (int64_t)B * Nv * ((S + mk::C - 1) / mk::C) * tk::CHUNK_ELEMS * 2;
     return 0;
 }
@@ -1112,14 +1132,15 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
 {
     *supported = true;
     ChunkParams pc = p;
-    if (dtype == 1) {
+    if (dtype == 1 || dtype == 2) {
         if (Dk == mk::DK && Dv == mk::DV && C == mk::C) {
+            const bool half = dtype == 2;
             // T of every chunk first, then the pass over the chunks.
             int nchk = (p.S + mk::C - 1) / mk::C;
             int tunits = p.B * p.Nv * nchk;
             if (tunits > 0) {
                 void *targs[] = {&pc, &nchk, &tunits};
-                const hipError_t e = hipLaunchKernel((const void *)chunk_t_kernel,
+                const hipError_t e = hipLaunchKernel(half ? (const void *)chunk_t_kernel<F16> : (const void *)chunk_t_kernel<BF16>,
                                                      dim3((tunits + tk::WAVES - 1) / tk::WAVES), dim3(64 * tk::WAVES),
                                                      targs, 0, s);
                 if (e != hipSuccess) return e;
@@ -1138,13 +1159,15 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
             if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
             const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
             if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-                for (const void *f : {(const void *)chunk_mfma_kernel<false>, (const void *)chunk_mfma_kernel<true>}) {
+                for (const void *f : {(const void *)chunk_mfma_kernel<BF16, false>, (const void *)chunk_mfma_kernel<BF16, true>,
+                                      (const void *)chunk_mfma_kernel<F16, false>, (const void *)chunk_mfma_kernel<F16, true>}) {
                     hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::LDS_BYTES);
                     if (e != hipSuccess) return e;
                 }
                 attr_done.fetch_or(bit, std::memory_order_acq_rel);
             }
-            const void *fn = pc.gate_a ? (const void *)chunk_mfma_kernel<true> : (const void *)chunk_mfma_kernel<false>;
+            const void *fn = half ? (pc.gate_a ? (const void *)chunk_mfma_kernel<F16, true> : (const void *)chunk_mfma_kernel<F16, false>)
+                                  : (pc.gate_a ? (const void *)chunk_mfma_kernel<BF16, true> : (const void *)chunk_mfma_kernel<BF16, false>);
             return hipLaunchKernel(fn, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);
         }
         *supported = false;

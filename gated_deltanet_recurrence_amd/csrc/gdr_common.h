@@ -85,17 +85,21 @@ hipError_t launch_norm(int dtype, const NormParams &p, hipStream_t s, bool *supp
 bool norm_supported(int Dv, int B, int Nv, int S);
 
 // ---------------------------------------------------------------------------
-// Element access helpers (device). bf16 values travel as raw 16-bit patterns;
-// widening is exact (shift into the high half of a float), narrowing rounds to
-// nearest even through the hardware converter.
+// Element access helpers (device). The 16-bit I/O formats are bf16 (8-bit
+// significand, float32's range) and IEEE fp16 (11-bit significand). Their
+// values travel as raw 16-bit patterns, two to a 32-bit word (the first in
+// the low half); widening to float32 is exact, narrowing rounds to nearest
+// even through the hardware converters.
 // ---------------------------------------------------------------------------
-typedef uint16_t bf16_t;
+typedef uint16_t bf16_t;   // bf16 storage (bit pattern)
+typedef _Float16 f16_t;    // fp16 storage
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // Two floats narrowed by one v_cvt_pk_bf16_f32 (a in the low half).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
@@ -103,8 +107,49 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// The two 16-bit formats behind one interface, for the kernels written for
+// either: lo / hi widen the elements of a word, pack narrows two floats into
+// one, dot2 is the hardware two-term dot product (exact products, float32
+// sum: v_dot2_f32_bf16 / v_dot2_f32_f16), to / from convert one element.
+struct BF16 {
+    typedef bf16_t T;
+    typedef __bf16 E;
+    static constexpr int dtype = 1;
+    static __device__ __forceinline__ float lo(uint32_t u) { return bf16_lo(u); }
+    static __device__ __forceinline__ float hi(uint32_t u) { return bf16_hi(u); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+    {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+    }
+    static __device__ __forceinline__ float to(uint32_t bits) { return __uint_as_float(bits << 16); }
+    static __device__ __forceinline__ uint16_t from(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+};
+struct F16 {
+    typedef f16_t T;
+    typedef _Float16 E;
+    static constexpr int dtype = 2;
+    static __device__ __forceinline__ float lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)u); }
+    static __device__ __forceinline__ float hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+    static __device__ __forceinline__ uint32_t pack(float a, float b)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+    }
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c)
+    {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+    }
+    static __device__ __forceinline__ float to(uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); }
+    static __device__ __forceinline__ uint16_t from(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+};
+// Trait of a storage type.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> { typedef BF16 type; };
+template <> struct Elem<f16_t> { typedef F16 type; };
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)x; }
 
 // Fused gates (the Gated DeltaNet blog post's layer code; inferencelayer
 // deltanet.rs, module header and its softplus): beta = sigmoid(b) and
@@ -142,6 +187,7 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x)
     __bf16 y = (__bf16)x;
     return __builtin_bit_cast(uint16_t, y);
 }
+template <> __device__ __forceinline__ f16_t from_f32<f16_t>(float x) { return (_Float16)x; }
 
 // Loads N consecutive elements (N * sizeof(T) in {4, 8, 16} bytes, aligned) as floats.
 template <typename T, int N> struct VecIO;
@@ -172,46 +218,49 @@ template <> struct VecIO<float, 1> {
     static __device__ __forceinline__ void load(const float *p, float *o) { o[0] = *p; }
     static __device__ __forceinline__ void store(float *p, const float *o) { *p = o[0]; }
 };
-template <> struct VecIO<bf16_t, 8> {
-    static __device__ __forceinline__ void load(const bf16_t *p, float *o)
+// 16-bit elements (bf16 or fp16), through their trait.
+template <typename T, int N, typename EL = typename Elem<T>::type> struct VecIO16;
+template <typename T, typename EL> struct VecIO16<T, 8, EL> {
+    static __device__ __forceinline__ void load(const T *p, float *o)
     {
         uint4 v = *reinterpret_cast<const uint4 *>(p);
-        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
-        o[4] = bf16_lo(v.z); o[5] = bf16_hi(v.z); o[6] = bf16_lo(v.w); o[7] = bf16_hi(v.w);
+        o[0] = EL::lo(v.x); o[1] = EL::hi(v.x); o[2] = EL::lo(v.y); o[3] = EL::hi(v.y);
+        o[4] = EL::lo(v.z); o[5] = EL::hi(v.z); o[6] = EL::lo(v.w); o[7] = EL::hi(v.w);
     }
-    static __device__ __forceinline__ void store(bf16_t *p, const float *o)
+    static __device__ __forceinline__ void store(T *p, const float *o)
     {
-        *reinterpret_cast<uint4 *>(p) = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
-                                                   pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+        *reinterpret_cast<uint4 *>(p) = make_uint4(EL::pack(o[0], o[1]), EL::pack(o[2], o[3]),
+                                                   EL::pack(o[4], o[5]), EL::pack(o[6], o[7]));
     }
 };
-template <> struct VecIO<bf16_t, 4> {
-    static __device__ __forceinline__ void load(const bf16_t *p, float *o)
+template <typename T, typename EL> struct VecIO16<T, 4, EL> {
+    static __device__ __forceinline__ void load(const T *p, float *o)
     {
         uint2 v = *reinterpret_cast<const uint2 *>(p);
-        o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+        o[0] = EL::lo(v.x); o[1] = EL::hi(v.x); o[2] = EL::lo(v.y); o[3] = EL::hi(v.y);
     }
-    static __device__ __forceinline__ void store(bf16_t *p, const float *o)
+    static __device__ __forceinline__ void store(T *p, const float *o)
     {
-        *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        *reinterpret_cast<uint2 *>(p) = make_uint2(EL::pack(o[0], o[1]), EL::pack(o[2], o[3]));
     }
 };
-template <> struct VecIO<bf16_t, 2> {
-    static __device__ __forceinline__ void load(const bf16_t *p, float *o)
+template <typename T, typename EL> struct VecIO16<T, 2, EL> {
+    static __device__ __forceinline__ void load(const T *p, float *o)
     {
         uint32_t v = *reinterpret_cast<const uint32_t *>(p);
-        o[0] = bf16_lo(v); o[1] = bf16_hi(v);
+        o[0] = EL::lo(v); o[1] = EL::hi(v);
     }
-    static __device__ __forceinline__ void store(bf16_t *p, const float *o)
+    static __device__ __forceinline__ void store(T *p, const float *o)
     {
-        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(o[0], o[1]);
+        *reinterpret_cast<uint32_t *>(p) = EL::pack(o[0], o[1]);
     }
 };
-
-template <> struct VecIO<bf16_t, 1> {
-    static __device__ __forceinline__ void load(const bf16_t *p, float *o) { o[0] = to_f32(*p); }
-    static __device__ __forceinline__ void store(bf16_t *p, const float *o) { *p = from_f32<bf16_t>(o[0]); }
+template <typename T, typename EL> struct VecIO16<T, 1, EL> {
+    static __device__ __forceinline__ void load(const T *p, float *o) { o[0] = to_f32(*p); }
+    static __device__ __forceinline__ void store(T *p, const float *o) { *p = from_f32<T>(o[0]); }
 };
+template <int N> struct VecIO<bf16_t, N> : VecIO16<bf16_t, N> {};
+template <int N> struct VecIO<f16_t, N> : VecIO16<f16_t, N> {};
 
 // Loads N consecutive elements with the widest aligned vector loads that fit
 // (N is a power of two; the address is aligned to min(N, 16 / sizeof(T)) elements).

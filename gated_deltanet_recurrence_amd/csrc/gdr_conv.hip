@@ -35,19 +35,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t conv_rsrc(const void *p, int64
 // reads past the bound return zeros, stores past it are dropped, so neither
 // needs a branch.
 template <typename T> struct Pair2;
-template <> struct Pair2<bf16_t> {
+template <typename T> struct Pair16 {
+    typedef typename Elem<T>::type EL;
     static __device__ __forceinline__ float2 load(__amdgpu_buffer_rsrc_t r, int off)
     {
         const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-        return make_float2(bf16_lo(u), bf16_hi(u));
+        return make_float2(EL::lo(u), EL::hi(u));
     }
     static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float2 v)
     {
-        __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v.x, v.y), r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(EL::pack(v.x, v.y), r, off, 0, 0);
     }
-    static __device__ __forceinline__ float one(const bf16_t *p) { return to_f32(*p); }
-    static __device__ __forceinline__ void put(bf16_t *p, float v) { *p = from_f32<bf16_t>(v); }
+    static __device__ __forceinline__ float one(const T *p) { return to_f32(*p); }
+    static __device__ __forceinline__ void put(T *p, float v) { *p = from_f32<T>(v); }
 };
+template <> struct Pair2<bf16_t> : Pair16<bf16_t> {};
+template <> struct Pair2<f16_t> : Pair16<f16_t> {};
 template <> struct Pair2<float> {
     static __device__ __forceinline__ float2 load(__amdgpu_buffer_rsrc_t r, int off)
     {
@@ -263,7 +266,8 @@ template <typename T, int K> struct DecodeK { static constexpr auto fn = conv_de
 hipError_t launch_conv_prefill(int dtype, const ConvParams &p, hipStream_t s, bool *supported)
 {
     const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
-    const void *fn = dtype == 1 ? conv_fn<PrefillK, bf16_t>(p.K) : conv_fn<PrefillK, float>(p.K);
+    const void *fn = dtype == 1 ? conv_fn<PrefillK, bf16_t>(p.K)
+                                : (dtype == 2 ? conv_fn<PrefillK, f16_t>(p.K) : conv_fn<PrefillK, float>(p.K));
     *supported = fn != nullptr;
     if (!fn) return hipSuccess;
     ConvParams pc = p;
@@ -276,7 +280,8 @@ hipError_t launch_conv_prefill(int dtype, const ConvParams &p, hipStream_t s, bo
 hipError_t launch_conv_decode(int dtype, const ConvParams &p, hipStream_t s, bool *supported)
 {
     const int C = 2 * p.Nk * p.Dk + p.Nv * p.Dv;
-    const void *fn = dtype == 1 ? conv_fn<DecodeK, bf16_t>(p.K) : conv_fn<DecodeK, float>(p.K);
+    const void *fn = dtype == 1 ? conv_fn<DecodeK, bf16_t>(p.K)
+                                : (dtype == 2 ? conv_fn<DecodeK, f16_t>(p.K) : conv_fn<DecodeK, float>(p.K));
     *supported = fn != nullptr;
     if (!fn) return hipSuccess;
     ConvParams pc = p;

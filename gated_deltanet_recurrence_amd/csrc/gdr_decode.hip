@@ -11,7 +11,7 @@
 // written once per call), so each wavefront owns one column tile of one
 // (b, h) state and keeps it in registers, in float32, across all tokens of
 // the call. The tile is TV columns wide: each lane holds VEC consecutive
-// columns (one 16-byte load for bf16) of RPL consecutive rows. The lanes that
+// columns (one 16-byte load for 16-bit types) of RPL consecutive rows. The lanes that
 // share a column group sit next to each other (row group = low lane bits), so
 // the two reductions over the key dimension (S^T k and S^T q) are a per-lane
 // sum over its rows followed by an all-reduce inside a 16-lane DPP row
@@ -209,7 +209,8 @@ __global__ __launch_bounds__(128) void decode_kernel(DecodeParams p)
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Decode step with one token per sequence (S = 1), bf16, Dk = Dv = 128.
+// Decode step with one token per sequence (S = 1), 16-bit I/O (bf16 or fp16),
+// Dk = Dv = 128.
 //
 // A workgroup of eight wavefronts updates one head at a time and walks the
 // heads g, g + G, g + 2G, ... (G workgroups, persistent). Wave j owns the
@@ -244,17 +245,17 @@ constexpr int NB = GDR_S1_NB;         // heads whose loads are in flight
 }  // namespace s1
 
 // Scalars of a head, read through the scalar cache ahead of use: beta (or its
-// logit) and, with fused gates, a as bf16 pairs; A_log and dt_bias of the head.
+// logit) and, with fused gates, a as 16-bit pairs; A_log and dt_bias of the head.
 struct S1Scal { int32_t len, nacc, idx, beta2, g, alog = 0, dtb = 0; };
 // One head's loads and resolution (r < 0: nothing to do).
 struct S1Head {
     int b, h, r;
     float beta, g;
-    u32x4_t st[s1::NI];   // 8 bf16 columns of each of the lane's rows
-    u32x2_t k, q;         // the lane's 4 rows of k and q (bf16)
-    u32x4_t v;            // the lane's 8 columns of v (bf16)
+    u32x4_t st[s1::NI];   // 8 16-bit columns of each of the lane's rows
+    u32x2_t k, q;         // the lane's 4 rows of k and q (16-bit)
+    u32x4_t v;            // the lane's 8 columns of v (16-bit)
     u32x4_t gk;           // the lane's 4 rows of gk (f32)
-    uint32_t z;           // the epilogue's z at the lane's two output columns (bf16)
+    uint32_t z;           // the epilogue's z at the lane's two output columns (16-bit)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t brsrc(const void *p, int bytes)
@@ -271,6 +272,7 @@ __device__ __forceinline__ float dpp_add(float x)
 // lane (o0, o1 at the columns of z's two halves, weights w0, w1): the sum of
 // squares over the 16 lanes of a row (quad swaps, then the mirrored half and
 // row), then over the four rows.
+template <typename EL>
 __device__ __forceinline__ uint32_t norm_pair(float o0, float o1, uint32_t z, float w0, float w1, float eps);
 
 // Sum over the four 16-lane rows of a wave, in every lane.
@@ -282,6 +284,7 @@ __device__ __forceinline__ float rows_sum(float x)
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+template <typename EL>
 __device__ __forceinline__ uint32_t norm_pair(float o0, float o1, uint32_t z, float w0, float w1, float eps)
 {
     float x = o0 * o0 + o1 * o1;
@@ -290,7 +293,7 @@ __device__ __forceinline__ uint32_t norm_pair(float o0, float o1, uint32_t z, fl
     x = dpp_add<0x141, 0xf>(x);   // row_half_mirror
     x = dpp_add<0x140, 0xf>(x);   // row_mirror
     const float r = norm_rinv(rows_sum(x), 128, eps);
-    return pack_bf16x2(o0 * r * w0 * norm_silu(bf16_lo(z)), o1 * r * w1 * norm_silu(bf16_hi(z)));
+    return EL::pack(o0 * r * w0 * norm_silu(EL::lo(z)), o1 * r * w1 * norm_silu(EL::hi(z)));
 }
 
 // Transposing reduction over the four 16-lane rows: given per-lane partials
@@ -326,7 +329,7 @@ __device__ __forceinline__ void s1_barrier()
 // GK: per-key decay gk given. FG: fused gates, beta and g formed in the
 // kernel from the logits and the raw gate input a. QN: q and k normalised in
 // the kernel. NRM: gated RMSNorm epilogue on the outputs (norm_pair).
-template <bool GK, bool FG, bool QN, bool NRM>
+template <typename EL, bool GK, bool FG, bool QN, bool NRM>
 __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, int nheads)
 {
     using namespace s1;
@@ -340,13 +343,13 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
     const int lr = lane >> 4, cg = lane & 15;
     const int row0 = j * RW + lr * NI;   // the lane's first row
 
-    const bf16_t *q = static_cast<const bf16_t *>(p.q);
-    const bf16_t *k = static_cast<const bf16_t *>(p.k);
-    const bf16_t *v = static_cast<const bf16_t *>(p.v);
-    bf16_t *pool = static_cast<bf16_t *>(p.pool);
-    bf16_t *out = static_cast<bf16_t *>(p.out);
+    const uint16_t *q = static_cast<const uint16_t *>(p.q);
+    const uint16_t *k = static_cast<const uint16_t *>(p.k);
+    const uint16_t *v = static_cast<const uint16_t *>(p.v);
+    uint16_t *pool = static_cast<uint16_t *>(p.pool);
+    uint16_t *out = static_cast<uint16_t *>(p.out);
     // Gated RMSNorm epilogue (NRM): z of each head's row, w of the lane's columns.
-    const bf16_t *zsrc = static_cast<const bf16_t *>(p.norm_z);
+    const uint16_t *zsrc = static_cast<const uint16_t *>(p.norm_z);
     float nw0 = 0.f, nw1 = 0.f;
     if constexpr (NRM) {
         const u32x2_t nwv = __builtin_amdgcn_raw_buffer_load_b64(brsrc(p.norm_w, DV * 4), (cg * 8 + lr * 2) * 4, 0, 0);
@@ -385,10 +388,10 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         const int n = p.nacc ? c.nacc : L;
         const int r = (hd < nheads && L == 1 && n == 1) ? c.idx : -1;
         H.r = (r >= 0 && r < p.slots) ? r : -1;
-        const float braw = __uint_as_float(((uint32_t)c.beta2 >> (16 * (vh & 1))) << 16);
+        const float braw = EL::to((uint32_t)c.beta2 >> (16 * (vh & 1)));
         H.beta = FG ? gate_sigmoid(braw) : braw;
         if constexpr (FG)
-            H.g = gate_g(__uint_as_float(((uint32_t)c.g >> (16 * (vh & 1))) << 16), __int_as_float(c.alog), __int_as_float(c.dtb));
+            H.g = gate_g(EL::to((uint32_t)c.g >> (16 * (vh & 1))), __int_as_float(c.alog), __int_as_float(c.dtb));
         else
             H.g = p.g ? __int_as_float(c.g) : 0.f;
         const bool on = H.r >= 0;
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
 #pragma unroll
             for (int i = 0; i < NI; ++i) dd[i] = a;
         }
-        const float kr[NI] = {bf16_lo(H.k.x), bf16_hi(H.k.x), bf16_lo(H.k.y), bf16_hi(H.k.y)};
+        const float kr[NI] = {EL::lo(H.k.x), EL::hi(H.k.x), EL::lo(H.k.y), EL::hi(H.k.y)};
         // Partial S^T (D k) and S^T (D q) over the lane's rows.
         uint32_t sw[NI][4];
         float kv[8], sq[8], kq = 0.f;
@@ -448,7 +451,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
 #pragma unroll
         for (int i = 0; i < NI; ++i) { sw[i][0] = H.st[i].x; sw[i][1] = H.st[i].y; sw[i][2] = H.st[i].z; sw[i][3] = H.st[i].w; }
         if constexpr (GK) {
-            const float qr[NI] = {bf16_lo(H.q.x), bf16_hi(H.q.x), bf16_lo(H.q.y), bf16_hi(H.q.y)};
+            const float qr[NI] = {EL::lo(H.q.x), EL::hi(H.q.x), EL::lo(H.q.y), EL::hi(H.q.y)};
             float dk[NI], dq[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
@@ -460,27 +463,28 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
             for (int i = 0; i < NI; ++i)
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
-                    const float s = (c & 1) ? bf16_hi(sw[i][c >> 1]) : bf16_lo(sw[i][c >> 1]);
+                    const float s = (c & 1) ? EL::hi(sw[i][c >> 1]) : EL::lo(sw[i][c >> 1]);
                     kv[c] = fmaf(s, dk[i], kv[c]);
                     sq[c] = fmaf(s, dq[i], sq[c]);
                 }
         } else {
-            // One decay for all rows: the sums run over bf16 pairs of rows
-            // (v_dot2_f32_bf16, exact products) and take exp(g) afterwards.
+            // One decay for all rows: the sums run over 16-bit pairs of rows
+            // (v_dot2_f32_bf16 / v_dot2_f32_f16, exact products) and take
+            // exp(g) afterwards.
             const uint32_t kp[2] = {H.k.x, H.k.y}, qp[2] = {H.q.x, H.q.y};
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
-                const bf16x2_t kb = __builtin_bit_cast(bf16x2_t, kp[pr]), qb = __builtin_bit_cast(bf16x2_t, qp[pr]);
-                kq = __builtin_amdgcn_fdot2_f32_bf16(kb, qb, kq, false);
+                const uint32_t kb = kp[pr], qb = qp[pr];
+                kq = EL::dot2(kb, qb, kq);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     // (S[2pr][2u], S[2pr+1][2u]) and (S[2pr][2u+1], S[2pr+1][2u+1])
-                    const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(sw[2 * pr + 1][u], sw[2 * pr][u], 0x05040100u));
-                    const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(sw[2 * pr + 1][u], sw[2 * pr][u], 0x07060302u));
-                    kv[2 * u] = __builtin_amdgcn_fdot2_f32_bf16(lo, kb, kv[2 * u], false);
-                    sq[2 * u] = __builtin_amdgcn_fdot2_f32_bf16(lo, qb, sq[2 * u], false);
-                    kv[2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, kb, kv[2 * u + 1], false);
-                    sq[2 * u + 1] = __builtin_amdgcn_fdot2_f32_bf16(hi, qb, sq[2 * u + 1], false);
+                    const uint32_t lo = __builtin_amdgcn_perm(sw[2 * pr + 1][u], sw[2 * pr][u], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(sw[2 * pr + 1][u], sw[2 * pr][u], 0x07060302u);
+                    kv[2 * u] = EL::dot2(lo, kb, kv[2 * u]);
+                    sq[2 * u] = EL::dot2(lo, qb, sq[2 * u]);
+                    kv[2 * u + 1] = EL::dot2(hi, kb, kv[2 * u + 1]);
+                    sq[2 * u + 1] = EL::dot2(hi, qb, sq[2 * u + 1]);
                 }
             }
         }
@@ -494,7 +498,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         // |k|^2 and |q|^2 for the in-kernel normalisation.
         float kk = 0.f, qq = 0.f;
         if constexpr (QN) {
-            const float qr[NI] = {bf16_lo(H.q.x), bf16_hi(H.q.x), bf16_lo(H.q.y), bf16_hi(H.q.y)};
+            const float qr[NI] = {EL::lo(H.q.x), EL::hi(H.q.x), EL::lo(H.q.y), EL::hi(H.q.y)};
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 kk = fmaf(kr[i], kr[i], kk);
@@ -542,13 +546,13 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         }
         // delta of this lane row's two columns, then of all eight.
         const uint32_t vw = lr == 0 ? H.v.x : lr == 1 ? H.v.y : lr == 2 ? H.v.z : H.v.w;
-        const float d0 = H.beta * (bf16_lo(vw) - u.x), d1 = H.beta * (bf16_hi(vw) - u.y);
+        const float d0 = H.beta * (EL::lo(vw) - u.x), d1 = H.beta * (EL::hi(vw) - u.y);
         if (j == 0) {
             const float o0 = p.scale * fmaf(d0, kq, u.z), o1 = p.scale * fmaf(d1, kq, u.w);
             if constexpr (NRM)
-                *out_ptr(H) = norm_pair(o0, o1, H.z, nw0, nw1, p.norm_eps);
+                *out_ptr(H) = norm_pair<EL>(o0, o1, H.z, nw0, nw1, p.norm_eps);
             else
-                *out_ptr(H) = pack_bf16x2(o0, o1);
+                *out_ptr(H) = EL::pack(o0, o1);
         }
         float e0[4], e1[4], dl[8];
         rows_gather(d0, e0);
@@ -565,8 +569,8 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
             uint32_t ow[4];
 #pragma unroll
             for (int c = 0; c < 8; c += 2)
-                ow[c >> 1] = pack_bf16x2(fmaf(bf16_lo(sw[i][c >> 1]), dd[i], kr[i] * dl[c]),
-                                         fmaf(bf16_hi(sw[i][c >> 1]), dd[i], kr[i] * dl[c + 1]));
+                ow[c >> 1] = EL::pack(fmaf(EL::lo(sw[i][c >> 1]), dd[i], kr[i] * dl[c]),
+                                         fmaf(EL::hi(sw[i][c >> 1]), dd[i], kr[i] * dl[c + 1]));
             __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, srs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
         }
     };
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
     }
 }
 
-// Decode calls of two to eight tokens per sequence (speculative steps), bf16,
+// Decode calls of two to eight tokens per sequence (speculative steps), bf16 or fp16,
 // Dk = Dv = 128. One workgroup of four wavefronts per (b, h): wave j owns the
 // 32 rows [32j, 32j + 32) of the state, lane l the columns 8 (l % 16) .. + 7
 // of the eight consecutive rows 32j + 8 (l / 16) + i, so that each load or
@@ -626,15 +630,15 @@ constexpr int NI = RW / 4;       // 8 rows per lane
 
 // One token's inputs as a lane holds them.
 struct MTTok {
-    u32x4_t k, q;        // the lane's 8 rows of k and q (bf16)
-    u32x4_t v;           // the lane's 8 columns of v (bf16)
+    u32x4_t k, q;        // the lane's 8 rows of k and q (16-bit)
+    u32x4_t v;           // the lane's 8 columns of v (16-bit)
     u32x4_t gk0, gk1;    // the lane's 8 rows of gk (f32)
-    uint32_t beta, g;    // bf16 in the low half (beta or its logit; a); g as f32 bits
-    uint32_t z;          // the epilogue's z at the lane's two output columns (bf16)
+    uint32_t beta, g;    // 16-bit in the low half (beta or its logit; a); g as f32 bits
+    uint32_t z;          // the epilogue's z at the lane's two output columns (16-bit)
     int w;               // the token's write slot
 };
 
-template <bool GK, bool FG, bool QN, bool NRM>
+template <typename EL, bool GK, bool FG, bool QN, bool NRM>
 __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK && (FG || QN)) || NRM ? 3 : 4))) void decode_mt_kernel(DecodeParams p)
 {
     using namespace mt;
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
     int r = -1;
     if (L > 0 && n >= 1 && n <= S) r = ld_const(p.idx, (size_t)b * S + n - 1);
     // Output words of this lane in wave 0: columns 8 cg + 2 lr, + 1 of each token.
-    uint32_t *optr = reinterpret_cast<uint32_t *>(static_cast<bf16_t *>(p.out) + vh * S * DV + cg * 8 + lr * 2);
+    uint32_t *optr = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(p.out) + vh * S * DV + cg * 8 + lr * 2);
     if (r < 0 || r >= p.slots) {
         if (j == 0)
             for (int t = 0; t < S; ++t) optr[t * (DV / 2)] = 0u;
@@ -664,18 +668,18 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
 
     // Token inputs through buffer resources bounded by the valid tokens: the
     // prefetch past the last one reads zeros.
-    const auto krs = brsrc(static_cast<const bf16_t *>(p.k) + qk * S * DK, L * DK * 2);
-    const auto qrs = brsrc(static_cast<const bf16_t *>(p.q) + qk * S * DK, L * DK * 2);
-    const auto vrs = brsrc(static_cast<const bf16_t *>(p.v) + vh * S * DV, L * DV * 2);
-    const auto brs = brsrc(static_cast<const bf16_t *>(p.beta) + vh * S, L * 2);
-    // g (float32), or with fused gates the raw a (bf16)
-    const auto grs = FG ? brsrc(static_cast<const bf16_t *>(p.gate_a) + vh * S, L * 2)
+    const auto krs = brsrc(static_cast<const uint16_t *>(p.k) + qk * S * DK, L * DK * 2);
+    const auto qrs = brsrc(static_cast<const uint16_t *>(p.q) + qk * S * DK, L * DK * 2);
+    const auto vrs = brsrc(static_cast<const uint16_t *>(p.v) + vh * S * DV, L * DV * 2);
+    const auto brs = brsrc(static_cast<const uint16_t *>(p.beta) + vh * S, L * 2);
+    // g (float32), or with fused gates the raw a (16-bit)
+    const auto grs = FG ? brsrc(static_cast<const uint16_t *>(p.gate_a) + vh * S, L * 2)
                         : brsrc(p.g ? p.g + vh * S : nullptr, p.g ? L * 4 : 0);
     const float alog = FG ? __int_as_float(ld_const(reinterpret_cast<const int32_t *>(p.A_log), h)) : 0.f;
     const float dtb = FG ? __int_as_float(ld_const(reinterpret_cast<const int32_t *>(p.dt_bias), h)) : 0.f;
     const auto gkrs = brsrc(GK ? p.gk + vh * S * DK : nullptr, GK ? L * DK * 4 : 0);
     // Gated RMSNorm epilogue (NRM): z of each token's row, w of the lane's columns.
-    const auto zrs = brsrc(NRM ? static_cast<const bf16_t *>(p.norm_z) + vh * S * DV : nullptr, NRM ? L * DV * 2 : 0);
+    const auto zrs = brsrc(NRM ? static_cast<const uint16_t *>(p.norm_z) + vh * S * DV : nullptr, NRM ? L * DV * 2 : 0);
     float nw0 = 0.f, nw1 = 0.f;
     if constexpr (NRM) {
         const u32x2_t nwv = __builtin_amdgcn_raw_buffer_load_b64(brsrc(p.norm_w, DV * 4), (cg * 8 + lr * 2) * 4, 0, 0);
@@ -703,7 +707,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
     ld_tok(cur, 0);
     float st[NI][8];
     {
-        const auto srs = brsrc(static_cast<const bf16_t *>(p.pool) + ((size_t)r * Nv + h) * DK * DV, DK * DV * 2);
+        const auto srs = brsrc(static_cast<const uint16_t *>(p.pool) + ((size_t)r * Nv + h) * DK * DV, DK * DV * 2);
         u32x4_t sw[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) sw[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
@@ -711,22 +715,22 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
         for (int i = 0; i < NI; ++i) {
             const uint32_t w4[4] = {sw[i].x, sw[i].y, sw[i].z, sw[i].w};
 #pragma unroll
-            for (int c = 0; c < 8; ++c) st[i][c] = (c & 1) ? bf16_hi(w4[c >> 1]) : bf16_lo(w4[c >> 1]);
+            for (int c = 0; c < 8; ++c) st[i][c] = (c & 1) ? EL::hi(w4[c >> 1]) : EL::lo(w4[c >> 1]);
         }
     }
-    bf16_t *pool = static_cast<bf16_t *>(p.pool);
+    uint16_t *pool = static_cast<uint16_t *>(p.pool);
     int par = 0;
     for (int t = 0; t < L; ++t) {
         ld_tok(nxt, t + 1);
-        const float a = FG ? __expf(gate_g(__uint_as_float(cur.g << 16), alog, dtb))
+        const float a = FG ? __expf(gate_g(EL::to(cur.g), alog, dtb))
                            : (p.g ? __expf(__uint_as_float(cur.g)) : 1.f);
         float dd[NI], kr[NI], qr[NI];
         {
             const uint32_t kw[4] = {cur.k.x, cur.k.y, cur.k.z, cur.k.w}, qw[4] = {cur.q.x, cur.q.y, cur.q.z, cur.q.w};
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
-                kr[i] = (i & 1) ? bf16_hi(kw[i >> 1]) : bf16_lo(kw[i >> 1]);
-                qr[i] = (i & 1) ? bf16_hi(qw[i >> 1]) : bf16_lo(qw[i >> 1]);
+                kr[i] = (i & 1) ? EL::hi(kw[i >> 1]) : EL::lo(kw[i >> 1]);
+                qr[i] = (i & 1) ? EL::hi(qw[i >> 1]) : EL::lo(qw[i >> 1]);
             }
             if constexpr (GK) {
                 const uint32_t gw[8] = {cur.gk0.x, cur.gk0.y, cur.gk0.z, cur.gk0.w, cur.gk1.x, cur.gk1.y, cur.gk1.z, cur.gk1.w};
@@ -807,15 +811,15 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
             u.x *= rk; u.y *= rk; u.z *= rq; u.w *= rq;
             kq *= rk * rq;
         }
-        const float beta = FG ? gate_sigmoid(__uint_as_float(cur.beta << 16)) : __uint_as_float(cur.beta << 16);
+        const float beta = FG ? gate_sigmoid(EL::to(cur.beta)) : EL::to(cur.beta);
         const uint32_t vw = lr == 0 ? cur.v.x : lr == 1 ? cur.v.y : lr == 2 ? cur.v.z : cur.v.w;
-        const float d0 = beta * (bf16_lo(vw) - u.x), d1 = beta * (bf16_hi(vw) - u.y);
+        const float d0 = beta * (EL::lo(vw) - u.x), d1 = beta * (EL::hi(vw) - u.y);
         if (j == 0) {
             const float o0 = p.scale * fmaf(d0, kq, u.z), o1 = p.scale * fmaf(d1, kq, u.w);
             if constexpr (NRM)
-                optr[t * (DV / 2)] = norm_pair(o0, o1, cur.z, nw0, nw1, p.norm_eps);
+                optr[t * (DV / 2)] = norm_pair<EL>(o0, o1, cur.z, nw0, nw1, p.norm_eps);
             else
-                optr[t * (DV / 2)] = pack_bf16x2(o0, o1);
+                optr[t * (DV / 2)] = EL::pack(o0, o1);
         }
         float e0[4], e1[4], dl[8];
         rows_gather(d0, e0);
@@ -836,7 +840,7 @@ __global__ __launch_bounds__(64 * mt::NW) __attribute__((amdgpu_waves_per_eu((GK
             for (int i = 0; i < NI; ++i) {
                 uint32_t ow[4];
 #pragma unroll
-                for (int c = 0; c < 8; c += 2) ow[c >> 1] = pack_bf16x2(st[i][c], st[i][c + 1]);
+                for (int c = 0; c < 8; c += 2) ow[c >> 1] = EL::pack(st[i][c], st[i][c + 1]);
                 __builtin_amdgcn_raw_buffer_store_b128(u32x4_t{ow[0], ow[1], ow[2], ow[3]}, wrs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
             }
         }
@@ -884,6 +888,37 @@ static hipError_t launch_typed(int Dk, int Dv, const DecodeParams &p, hipStream_
     return hipSuccess;
 }
 
+// The compiled variant for a call: per-key gate, fused gates, q/k
+// normalisation, epilogue.
+template <typename EL>
+static const void *s1_kernel(const DecodeParams &p)
+{
+    static const void *const fns[16] = {
+        (const void *)decode_s1_kernel<EL, false, false, false, false>, (const void *)decode_s1_kernel<EL, true, false, false, false>,
+        (const void *)decode_s1_kernel<EL, false, true, false, false>, (const void *)decode_s1_kernel<EL, true, true, false, false>,
+        (const void *)decode_s1_kernel<EL, false, false, true, false>, (const void *)decode_s1_kernel<EL, true, false, true, false>,
+        (const void *)decode_s1_kernel<EL, false, true, true, false>, (const void *)decode_s1_kernel<EL, true, true, true, false>,
+        (const void *)decode_s1_kernel<EL, false, false, false, true>, (const void *)decode_s1_kernel<EL, true, false, false, true>,
+        (const void *)decode_s1_kernel<EL, false, true, false, true>, (const void *)decode_s1_kernel<EL, true, true, false, true>,
+        (const void *)decode_s1_kernel<EL, false, false, true, true>, (const void *)decode_s1_kernel<EL, true, false, true, true>,
+        (const void *)decode_s1_kernel<EL, false, true, true, true>, (const void *)decode_s1_kernel<EL, true, true, true, true>};
+    return fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
+}
+template <typename EL>
+static const void *mt_kernel(const DecodeParams &p)
+{
+    static const void *const fns[16] = {
+        (const void *)decode_mt_kernel<EL, false, false, false, false>, (const void *)decode_mt_kernel<EL, true, false, false, false>,
+        (const void *)decode_mt_kernel<EL, false, true, false, false>, (const void *)decode_mt_kernel<EL, true, true, false, false>,
+        (const void *)decode_mt_kernel<EL, false, false, true, false>, (const void *)decode_mt_kernel<EL, true, false, true, false>,
+        (const void *)decode_mt_kernel<EL, false, true, true, false>, (const void *)decode_mt_kernel<EL, true, true, true, false>,
+        (const void *)decode_mt_kernel<EL, false, false, false, true>, (const void *)decode_mt_kernel<EL, true, false, false, true>,
+        (const void *)decode_mt_kernel<EL, false, true, false, true>, (const void *)decode_mt_kernel<EL, true, true, false, true>,
+        (const void *)decode_mt_kernel<EL, false, false, true, true>, (const void *)decode_mt_kernel<EL, true, false, true, true>,
+        (const void *)decode_mt_kernel<EL, false, true, true, true>, (const void *)decode_mt_kernel<EL, true, true, true, true>};
+    return fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
+}
+
 hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipStream_t s, bool *supported,
                          bool *norm_done)
 {
@@ -891,7 +926,7 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
     // decode_s1_kernel reads beta (and a) of two heads as one 32-bit word, so
     // it takes an even number of heads; odd counts go to decode_mt_kernel,
     // whose bounded 16-bit loads never read past the last head.
-    if (dtype == 1 && p.S == 1 && Dk == s1::DK && Dv == s1::DV && ((int64_t)p.B * p.Nv) % 2 == 0) {
+    if (dtype != 0 && p.S == 1 && Dk == s1::DK && Dv == s1::DV && ((int64_t)p.B * p.Nv) % 2 == 0) {
         *supported = true;
         *norm_done = true;
         const int nheads = p.B * p.Nv;
@@ -899,36 +934,19 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
         DecodeParams pc = p;
         int nh = nheads;
         void *args[] = {&pc, &nh};
-        static const void *const fns[16] = {
-            (const void *)decode_s1_kernel<false, false, false, false>, (const void *)decode_s1_kernel<true, false, false, false>,
-            (const void *)decode_s1_kernel<false, true, false, false>, (const void *)decode_s1_kernel<true, true, false, false>,
-            (const void *)decode_s1_kernel<false, false, true, false>, (const void *)decode_s1_kernel<true, false, true, false>,
-            (const void *)decode_s1_kernel<false, true, true, false>, (const void *)decode_s1_kernel<true, true, true, false>,
-            (const void *)decode_s1_kernel<false, false, false, true>, (const void *)decode_s1_kernel<true, false, false, true>,
-            (const void *)decode_s1_kernel<false, true, false, true>, (const void *)decode_s1_kernel<true, true, false, true>,
-            (const void *)decode_s1_kernel<false, false, true, true>, (const void *)decode_s1_kernel<true, false, true, true>,
-            (const void *)decode_s1_kernel<false, true, true, true>, (const void *)decode_s1_kernel<true, true, true, true>};
-        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
+        const void *fn = dtype == 1 ? s1_kernel<BF16>(p) : s1_kernel<F16>(p);
         return hipLaunchKernel(fn, grid, block, args, 0, s);
     }
-    if (dtype == 1 && Dk == mt::DK && Dv == mt::DV) {
+    if (dtype != 0 && Dk == mt::DK && Dv == mt::DV) {
         *supported = true;
         *norm_done = true;
         DecodeParams pc = p;
         void *args[] = {&pc};
-        static const void *const fns[16] = {
-            (const void *)decode_mt_kernel<false, false, false, false>, (const void *)decode_mt_kernel<true, false, false, false>,
-            (const void *)decode_mt_kernel<false, true, false, false>, (const void *)decode_mt_kernel<true, true, false, false>,
-            (const void *)decode_mt_kernel<false, false, true, false>, (const void *)decode_mt_kernel<true, false, true, false>,
-            (const void *)decode_mt_kernel<false, true, true, false>, (const void *)decode_mt_kernel<true, true, true, false>,
-            (const void *)decode_mt_kernel<false, false, false, true>, (const void *)decode_mt_kernel<true, false, false, true>,
-            (const void *)decode_mt_kernel<false, true, false, true>, (const void *)decode_mt_kernel<true, true, false, true>,
-            (const void *)decode_mt_kernel<false, false, true, true>, (const void *)decode_mt_kernel<true, false, true, true>,
-            (const void *)decode_mt_kernel<false, true, true, true>, (const void *)decode_mt_kernel<true, true, true, true>};
-        const void *fn = fns[(p.gk ? 1 : 0) + (p.gate_a ? 2 : 0) + (p.qk_norm ? 4 : 0) + (p.norm_z ? 8 : 0)];
+        const void *fn = dtype == 1 ? mt_kernel<BF16>(p) : mt_kernel<F16>(p);
         return hipLaunchKernel(fn, dim3((unsigned)(p.B * p.Nv)), dim3(64 * mt::NW), args, 0, s);
     }
     if (dtype == 1) return launch_typed<bf16_t>(Dk, Dv, p, s, supported);
+    if (dtype == 2) return launch_typed<f16_t>(Dk, Dv, p, s, supported);
     return launch_typed<float>(Dk, Dv, p, s, supported);
 }
 

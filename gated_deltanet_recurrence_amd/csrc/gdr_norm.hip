@@ -35,20 +35,23 @@ __device__ __forceinline__ float group_sum(float x)
 
 // Eight adjacent elements of a row (16 bytes in bf16, 32 in float).
 template <typename T> struct Oct;
-template <> struct Oct<bf16_t> {
-    static __device__ __forceinline__ void load(const bf16_t *p, float *x)
+template <typename T> struct Oct16 {
+    typedef typename Elem<T>::type EL;
+    static __device__ __forceinline__ void load(const T *p, float *x)
     {
         const u32x4_t u = *reinterpret_cast<const u32x4_t *>(p);
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { x[2 * i] = bf16_lo(w[i]); x[2 * i + 1] = bf16_hi(w[i]); }
+        for (int i = 0; i < 4; ++i) { x[2 * i] = EL::lo(w[i]); x[2 * i + 1] = EL::hi(w[i]); }
     }
-    static __device__ __forceinline__ void store(bf16_t *p, const float *x)
+    static __device__ __forceinline__ void store(T *p, const float *x)
     {
-        *reinterpret_cast<u32x4_t *>(p) = u32x4_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
-                                                  pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])};
+        *reinterpret_cast<u32x4_t *>(p) = u32x4_t{EL::pack(x[0], x[1]), EL::pack(x[2], x[3]),
+                                                  EL::pack(x[4], x[5]), EL::pack(x[6], x[7])};
     }
 };
+template <> struct Oct<bf16_t> : Oct16<bf16_t> {};
+template <> struct Oct<f16_t> : Oct16<f16_t> {};
 template <> struct Oct<float> {
     static __device__ __forceinline__ void load(const float *p, float *x)
     {
@@ -132,7 +135,9 @@ hipError_t launch_norm(int dtype, const NormParams &p, hipStream_t s, bool *supp
     const dim3 grid((unsigned)nwg), block(64 * NORM_WAVES);
     const void *fn = nullptr;
 #define GDR_NORM_CASE(D_)                                                                          \
-    if (p.Dv == D_) fn = dtype == 1 ? (const void *)norm_kernel<bf16_t, D_> : (const void *)norm_kernel<float, D_>;
+    if (p.Dv == D_)                                                                                \
+        fn = dtype == 1 ? (const void *)norm_kernel<bf16_t, D_>                                    \
+                        : (dtype == 2 ? (const void *)norm_kernel<f16_t, D_> : (const void *)norm_kernel<float, D_>);
     GDR_NORM_CASE(16) GDR_NORM_CASE(32) GDR_NORM_CASE(64) GDR_NORM_CASE(128)
 #undef GDR_NORM_CASE
     return hipLaunchKernel(fn, grid, block, args, 0, s);

@@ -22,8 +22,13 @@
  *  - The work is enqueued on `stream` (a hipStream_t; NULL = the legacy default
  *    stream). Device integers are never read by the host.
  *  - Element type `dtype` applies to q, k, v, beta, the states and out:
- *    GDR_BF16 (bfloat16, stored rounded to nearest even) or GDR_F32.
- *    g and gk are always float32. Integers are int32.
+ *    GDR_BF16 (bfloat16), GDR_F16 (IEEE half) or GDR_F32; 16-bit values are
+ *    stored rounded to nearest even, and all arithmetic runs in float32
+ *    (the states too) with 16-bit matrix-core operands in the I/O format.
+ *    The prefill operator page accepts bf16 and fp16 inputs and returns the
+ *    input's type (lite_boost.ops.chunk_gated_delta_rule, wrapper and note);
+ *    float32 serves small heads. g and gk are always float32. Integers are
+ *    int32.
  *  - Value head h uses key/query head h / (Nv / Nk): the repeat-interleave
  *    grouping of the blog post's layer code. Nv must be a multiple of Nk.
  *  - Fused gates (optional, both calls). Instead of beta and g, a caller may
@@ -86,7 +91,7 @@ typedef enum {
                                 than the library's fixed array holds (ValueError) */
 } gdr_status;
 
-typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1, GDR_F16 = 2 } gdr_dtype;
 
 /*
  * Recurrent decode over an indexed state pool.
@@ -122,7 +127,7 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *   a write slot outside [0, num_slots) skips that store only.
  *   Two sequences of one call must not share a slot (the result is undefined).
  *   A call is not idempotent: it advances the pool.
- * Supported: Dk, Dv in {16, 32, 64, 128}; both dtypes.
+ * Supported: Dk, Dv in {16, 32, 64, 128}; all three dtypes.
  * Errors: GDR_ERR_NULL if a is NULL or q, k, v, state_pool, out,
  *   actual_seq_lengths or ssm_state_indices is NULL, beta is NULL without
  *   fused gates, or one of the four fused-gate pointers is given without the
@@ -188,8 +193,8 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  * Inputs at positions t >= L_b are never read.
  * The result equals the token-by-token recurrence up to rounding; the state
  * is carried in float32 between chunks.
- * Supported: bf16 with Dk = Dv = 128 and chunk_size 64 (matrix-core path,
- *   which first forms (I + A)^-1 of every chunk in the workspace:
+ * Supported: bf16 or fp16 with Dk = Dv = 128 and chunk_size 64 (matrix-core
+ *   path, which first forms (I + A)^-1 of every chunk in the workspace:
  *   B * Nv * ceil(S / 64) * 8192 bytes); f32 with Dk = Dv in {16, 32} and
  *   chunk_size in {16, 32, 64}, or Dk = Dv = 64 and chunk_size in {16, 32}
  *   (no workspace).
@@ -315,7 +320,7 @@ GDR_API gdr_status gdr_conv_decode(const gdr_conv_decode_args *a, void *stream);
  * threads without ordering between them — race on it and must not overlap;
  * calls ordered on one stream are safe.
  * Limit: gdr_chunk_workspace_size(a) <= GDR_NOALLOC_SCRATCH_BYTES; for the
- * bf16 128/128 path that is B * Nv * ceil(S / 64) <= 8192 chunks (the chunked
+ * 16-bit 128/128 path that is B * Nv * ceil(S / 64) <= 8192 chunks (the chunked
  * prefill of B = 4, Nv = 32, S = 4096 exactly). f32 calls need no scratch.
  * Errors: those of gdr_chunk (without its workspace checks), then
  *   GDR_ERR_SCRATCH_LIMIT beyond the limit (nothing is enqueued), and
@@ -334,7 +339,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 6
+#define GDR_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -74,9 +74,12 @@ def _sigmoid(x):
 
 
 def _store(x, dtype):
-    """float array -> storage array: float32, or uint16 bf16 bit patterns."""
+    """float array -> storage array: float32, float16 (numpy rounds to nearest
+    even), or uint16 bf16 bit patterns."""
     if dtype == "f32":
         return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return np.ascontiguousarray(np.asarray(x, dtype=np.float32).astype(np.float16))
     return bf16_bits(np.asarray(x, dtype=np.float32))
 
 
@@ -91,9 +94,9 @@ def widen(x, dtype) -> Optional[np.ndarray]:
 
 @dataclass
 class Case:
-    """One seeded operator input. Storage arrays are float32 or uint16 (bf16 bits)."""
+    """One seeded operator input. Storage arrays are float32, float16, or uint16 (bf16 bits)."""
     kind: str                      # "decode" or "prefill"
-    dtype: str                     # "f32" or "bf16": q/k/v/beta/state/out
+    dtype: str                     # "f32", "bf16" or "f16": q/k/v/beta/state/out
     B: int
     Nk: int
     Nv: int
@@ -239,7 +242,7 @@ def conv_inputs(base, B, S, C, K, dtype, slots=None):
 def _poison(case: Case):
     """Puts NaN into every input position past each sequence's valid length."""
     L = case.valid_lengths()
-    nanv = BF16_NAN if case.dtype == "bf16" else np.float32(np.nan)
+    nanv = BF16_NAN if case.dtype == "bf16" else (np.float16(np.nan) if case.dtype == "f16" else np.float32(np.nan))
     for b in range(case.B):
         t0 = int(L[b])
         if t0 >= case.S:

@@ -10,7 +10,9 @@ import gated_deltanet_recurrence_amd as gdr
 import oracle
 import synth
 
-TOL = {"f32": 1e-4, "bf16": 2e-2}
+# max-abs bars: float32 and bf16 I/O as stated for the workloads; fp16 I/O
+# (the prefill operator's other accepted dtype) takes the bf16 bar.
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
 
 
 def say(msg):
@@ -32,7 +34,7 @@ def to_f64(t):
 
 
 def raw_bits(t):
-    if t.dtype == torch.bfloat16:
+    if t.element_size() == 2:
         return t.contiguous().view(torch.int16)
     return t.contiguous().view(torch.int32)
 

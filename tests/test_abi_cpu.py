@@ -132,6 +132,8 @@ _OPTION_CASES += [
     (dict(gk=FAKE + 4), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, num_state_indices=0, q=None, out=None), gdr.GDR_OK),
     (dict(beta=None), gdr.GDR_ERR_NULL),
+    (dict(dtype=3), gdr.GDR_ERR_DTYPE),
+    (dict(dtype=gdr.GDR_F16, Dk=96), gdr.GDR_ERR_UNSUPPORTED),
 ] + _OPTION_CASES)
 def test_decode_validation(lib, kw, code):
     a = _dec(**kw)
@@ -157,6 +159,10 @@ def test_decode_validation(lib, kw, code):
     (dict(S=1 << 23), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, q=None, out=None, workspace=None), gdr.GDR_OK),
     (dict(beta=None), gdr.GDR_ERR_NULL),
+    (dict(dtype=3), gdr.GDR_ERR_DTYPE),
+    (dict(dtype=gdr.GDR_F16, chunk_size=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dtype=gdr.GDR_F16, Dk=64, Dv=64), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dtype=gdr.GDR_F16, workspace=None), gdr.GDR_ERR_NULL),
 ] + _OPTION_CASES)
 def test_chunk_validation(lib, kw, code):
     a = _chk(**kw)
@@ -284,4 +290,5 @@ def test_chunk_workspace_size(lib):
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=128))) == 2 * 4 * 2 * 8192
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=0))) == 0
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F32, Dk=32, Dv=32, chunk_size=32))) == 0
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F16))) == 2 * 4 * 2 * 8192
     assert lib.gdr_chunk_workspace_size(None) == -1

@@ -36,7 +36,7 @@ import gated_deltanet_recurrence_amd as gdr
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-6
-REL = {"bf16": 2.0 ** -7, "f32": 1e-5}
+REL = {"bf16": 2.0 ** -7, "f16": 2.0 ** -10, "f32": 1e-5}
 
 
 def _norm_inputs(c, base, poison=False):
