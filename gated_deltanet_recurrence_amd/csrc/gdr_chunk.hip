@@ -582,7 +582,9 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 // reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
 // FG: fused gates (raw a and beta logits in place of g and beta).
-template <typename EL, bool FG>
+// ND: no decay (g absent, alpha = 1): every decay factor is 1, and the
+// multiplies by them are left out.
+template <typename EL, bool FG, bool ND>
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
     using namespace mk;
@@ -714,13 +716,18 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             for (int rb = 0; rb < 2; ++rb) vn[rb] += uu[rb];
             const float *vec = reinterpret_cast<const float *>(set + S_VEC);
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) ot[tb] *= vec[32 * tb + c32];
+            for (int tb = 0; tb < 2; ++tb) ot[tb] *= ND ? p.scale : vec[32 * tb + c32];
 
             // Vnew as the left operand of Vnew^T, and decayed as the right
             // operand of the state update.
             e16x8_t vna[4], vnb[4];
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) {
+                if constexpr (ND) {
+                    vna[2 * rb] = vnb[2 * rb] = op8<EL>(vn[rb], 0);
+                    vna[2 * rb + 1] = vnb[2 * rb + 1] = op8<EL>(vn[rb], 1);
+                    continue;
+                }
                 f32x16_t dv;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -754,9 +761,11 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                 }
             }
             // S <- exp(gamma_C) S0 + K^T (decayed Vnew).
-            const float egC = vec[128];
+            if constexpr (!ND) {
+                const float egC = vec[128];
 #pragma unroll
-            for (int f = 0; f < 4; ++f) st[f] *= egC;
+                for (int f = 0; f < 4; ++f) st[f] *= egC;
+            }
 #pragma unroll
             for (int f = 0; f < 4; ++f)
 #pragma unroll
@@ -822,8 +831,9 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     rt[n] = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + (ltid + 128 * n) * 16, 0, 0);
                 if constexpr (W == 1) {
                     rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
-                    rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
-                            : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
+                    if constexpr (!ND)
+                        rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
+                                : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
                 }
             }
         };
@@ -864,7 +874,14 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     *reinterpret_cast<u32x4_t *>(set + S_T + (ltid + 128 * n) * 16) = rt[n];
                     traw[n] = rt[n];
                 }
-                if constexpr (W == 1) {
+                if constexpr (W == 1 && ND) {
+                    // No decay: beta alone. The outputs need no per-row factor,
+                    // since rows past the length have zero q.
+                    const float beta = EL::to(rb);
+                    bg[lane] = beta;
+                    bg[64 + lane] = 0.f;
+                    bg[128 + lane] = beta;
+                } else if constexpr (W == 1) {
                     // Per-token factors of chunk cn (lane t = token t): gamma is the
                     // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
                     const int nv = min(C, L - cn * C);
@@ -910,13 +927,18 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     G = mfma32<EL>(ld8(set, S_KT + sw256t(32 * ibq + c32, 2 * ks + hh)),
                                ld8(set, S_Q + sw256(32 * rbq + c32, 2 * ks + hh)), G);
                 const int r = 32 * rbq + c32;
-                const float gq = gv[r];
-                float gi[16];
-                rows4(gv, 32 * ibq, gi);
+                if constexpr (ND) {
 #pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int i = 32 * ibq + drow(q, hh);
-                    G[q] = i <= r ? p.scale * __builtin_amdgcn_exp2f(gq - gi[q]) * G[q] : 0.f;
+                    for (int q = 0; q < 16; ++q) G[q] = 32 * ibq + drow(q, hh) <= r ? p.scale * G[q] : 0.f;
+                } else {
+                    const float gq = gv[r];
+                    float gi[16];
+                    rows4(gv, 32 * ibq, gi);
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int i = 32 * ibq + drow(q, hh);
+                        G[q] = i <= r ? p.scale * __builtin_amdgcn_exp2f(gq - gi[q]) * G[q] : 0.f;
+                    }
                 }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8<EL>(G, s));
@@ -1159,15 +1181,19 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
             if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
             const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
             if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-                for (const void *f : {(const void *)chunk_mfma_kernel<BF16, false>, (const void *)chunk_mfma_kernel<BF16, true>,
-                                      (const void *)chunk_mfma_kernel<F16, false>, (const void *)chunk_mfma_kernel<F16, true>}) {
+                for (const void *f : {(const void *)chunk_mfma_kernel<BF16, false, false>, (const void *)chunk_mfma_kernel<BF16, true, false>,
+                                      (const void *)chunk_mfma_kernel<BF16, false, true>, (const void *)chunk_mfma_kernel<F16, false, false>,
+                                      (const void *)chunk_mfma_kernel<F16, true, false>, (const void *)chunk_mfma_kernel<F16, false, true>}) {
                     hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::LDS_BYTES);
                     if (e != hipSuccess) return e;
                 }
                 attr_done.fetch_or(bit, std::memory_order_acq_rel);
             }
-            const void *fn = half ? (pc.gate_a ? (const void *)chunk_mfma_kernel<F16, true> : (const void *)chunk_mfma_kernel<F16, false>)
-                                  : (pc.gate_a ? (const void *)chunk_mfma_kernel<BF16, true> : (const void *)chunk_mfma_kernel<BF16, false>);
+            const bool nd = !pc.gate_a && !pc.g;
+            const void *fn = half ? (pc.gate_a ? (const void *)chunk_mfma_kernel<F16, true, false>
+                                               : (nd ? (const void *)chunk_mfma_kernel<F16, false, true> : (const void *)chunk_mfma_kernel<F16, false, false>))
+                                  : (pc.gate_a ? (const void *)chunk_mfma_kernel<BF16, true, false>
+                                               : (nd ? (const void *)chunk_mfma_kernel<BF16, false, true> : (const void *)chunk_mfma_kernel<BF16, false, false>));
             return hipLaunchKernel(fn, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);
         }
         *supported = false;

@@ -135,3 +135,10 @@ def test_qk_norm_prefill_fp32():
     c = synth.prefill_case(B=2, Nk=1, Nv=2, S=100, Dk=32, Dv=32, dtype="f32", base=625, lens=[100, 37],
                            chunk=32, scale=0.3, init_std=0.1)
     _chunk(c, 625, gates=False, qk_norm=True)
+
+
+def test_qk_norm_prefill_no_decay():
+    # g absent takes the kernel variant without decay factors; rows past each
+    # length must still come out zero with normalised (zero) q rows there
+    c = synth.config(5, B=3, Nk=2, Nv=4, S=300, lens=[300, 129, 1], base=626)
+    _chunk(c, 626, gates=False, qk_norm=True)
