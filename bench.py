@@ -97,6 +97,7 @@ def measured_traffic(profile, kind, entry=None):
 FUSED_PROFILE = "fused_gates_decode_step_and_chunked_prefill.txt"
 NORM_PROFILE = "epilogue_kernels_decode_step_and_chunked_prefill.txt"
 CONV_PROFILE = "conv_kernels_prefill_and_decode_step.txt"
+F16_PROFILE = "f16_decode_step_and_chunked_prefill.txt"
 
 
 # ---------------------------------------------------------------------------
@@ -159,6 +160,9 @@ def prefill_work(c, fused=False, norm=False):
 WARM_S = 0.3   # untimed warm-up of at least this long before every timed run
 
 
+GRAPH_MIN_LAUNCHES = 64
+
+
 def time_calls(calls, steps, warmup, use_graph):
     """Runs `warmup` then `steps` calls (cycling through `calls`), timed with
     HIP events on the current stream. Returns (ms per call by events, wall s).
@@ -172,10 +176,16 @@ def time_calls(calls, steps, warmup, use_graph):
         for i in range(n):
             calls[i]()                               # first launch outside capture
         torch.cuda.synchronize()
+        # A graph holds at least GRAPH_MIN_LAUNCHES calls (the list repeated),
+        # so that the host's cost of one replay stays below the GPU time it
+        # launches, also for calls of a few microseconds.
+        rounds = max(1, math.ceil(GRAPH_MIN_LAUNCHES / n))
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for i in range(n):
-                calls[i]()
+            for _ in range(rounds):
+                for i in range(n):
+                    calls[i]()
+        n *= rounds
         reps_w = max(1, math.ceil(warmup / n))
         t_w = time.perf_counter()
         for _ in range(reps_w):
@@ -475,7 +485,8 @@ def main():
                           "state_GBps": state_b / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "decode_s1_kernel (fp16)", "bound": "hbm", "achieved": gbs,
                                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                                       "traffic": None, "algorithmic_bytes_per_launch": bytes_call}})
+                                       "traffic": measured_traffic(F16_PROFILE, "decode", "decode step"),
+                                       "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls
         torch.cuda.empty_cache()
         log("chunked prefill workload, fp16")
@@ -490,7 +501,8 @@ def main():
                           "TFLOPs": tf, "GBps": bytes_call / (ms * 1e-3) / 1e9,
                           "roofline": {"kernel": "chunk_t_kernel + chunk_mfma_kernel (fp16)", "bound": "mfma",
                                        "achieved": tf, "peak": F16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                       "frac": tf / F16_MFMA_PEAK_TFLOPS, "traffic": None,
+                                       "frac": tf / F16_MFMA_PEAK_TFLOPS,
+                                       "traffic": measured_traffic(F16_PROFILE, "chunk", "chunked prefill"),
                                        "algorithmic_flops_per_launch": flops,
                                        "algorithmic_bytes_per_launch": bytes_call}})
         del keep, calls, c
