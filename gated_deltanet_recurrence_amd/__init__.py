@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_OK, GDR_ERR_NULL, GDR_ERR_SHAPE, GDR_ERR_DTYPE, GDR_ERR_UNSUPPORTED, GDR_ERR_LAUNCH, GDR_ERR_SCRATCH_LIMIT = range(7)
-GDR_NOALLOC_SCRATCH_BYTES = 64 << 20
+GDR_NOALLOC_SCRATCH_BYTES = 48 << 20
 GDR_F32, GDR_BF16, GDR_F16 = 0, 1, 2
 
 _vp = ctypes.c_void_p

@@ -181,26 +181,33 @@ namespace mk {
 constexpr int C = 64;          // chunk length
 constexpr int DK = 128;        // key head size
 constexpr int DV = 128;        // value head size
-constexpr int DVT = 64;        // value columns per workgroup
-constexpr int NT = DV / DVT;   // column tiles per head
-constexpr int NPREP = 6;       // wavefronts building the chunk operands
-constexpr int NTHR = 512;      // 6 prep + 2 chain wavefronts
+constexpr int NTHR = 512;      // 8 wavefronts: prep waves, then chain waves
+// Heads from which a workgroup takes a whole head (NT = 1) rather than half
+// of its value columns (NT = 2): two per CU of a 256-CU chip.
+constexpr int WHOLE_ROW_HEADS = 512;
 // Operand set of one chunk (double-buffered: the chain consumes chunk c while
 // the prep waves build chunk c + 1). Byte offsets within a set:
 constexpr int S_Q = 0;         // Q rows, features in k-order             [64][256 B]
 constexpr int S_KT = 16384;    // K rows, features in k-order             [64][256 B] (read transposed)
 constexpr int S_W = 32768;     // -W rows, features in k-order            [64][256 B]
 constexpr int S_P = 49152;     // P rows, tokens in k-order               [64][128 B]
-constexpr int S_VT = 57344;    // V rows, columns in k-order              [64][128 B] (read transposed)
-constexpr int S_T = 65536;     // T as written by chunk_t_kernel          [6][64][16 B]
-constexpr int S_TB = 71680;    // T diag(beta) in the same order          [6][64][16 B]
-constexpr int S_VEC = 77824;   // scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64], exp(gamma_C)
-constexpr int SET_BYTES = 78848;
-// Prep-only buffers.
-constexpr int P_BG = 2 * SET_BYTES;  // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
-constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
-constexpr int LDS_BYTES = P_FLAG + 64;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+constexpr int S_VT = 57344;    // V rows (NT = 1: diag(beta) V), columns in k-order [64][2 DVT B] (read transposed)
+// The rest depends on NT, the column tiles per head.
+template <int NT> struct Tile {
+    static constexpr int DVT = DV / NT;          // value columns per workgroup
+    static constexpr int NCHAIN = DVT / 32;      // chain wavefronts, 32 state columns each
+    static constexpr int NPREP = 8 - NCHAIN;     // wavefronts building the chunk operands
+    static constexpr int S_T = S_VT + 64 * 2 * DVT;          // T as chunk_t_kernel wrote it [6][64][16 B]
+    static constexpr int S_TB = S_T + 6144;                  // NT = 2: T diag(beta), same order
+    static constexpr int S_VEC = NT == 2 ? S_TB + 6144 : S_T + 6144;
+    // S_VEC: scale exp(gamma_t) (0 past the length) [64], exp(gamma_C - gamma_t) [64], exp(gamma_C)
+    static constexpr int SET_BYTES = S_VEC + 1024;
+    // Prep-only buffers.
+    static constexpr int P_BG = 2 * SET_BYTES;  // beta, gamma log2(e), beta exp(gamma) [3][64] of the chunk being built
+    static constexpr int P_FLAG = P_BG + 768;   // arrival counters of the prep waves
+    static constexpr int LDS_BYTES = P_FLAG + 64;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
 }  // namespace mk
 
 // Synchronisation inside the workgroup orders LDS only. Waves never pass
@@ -308,11 +315,11 @@ __device__ __forceinline__ void wait_for(uint32_t *f, uint32_t target)
 // T is stored in result-register order, so that every store is 1 KB
 // contiguous: per chunk, block j (0: T_00, 1: T_11, 2: T_10) and k-step s hold
 // op8 of D(T_j^T): row r = c32 of the block holds columns (k-order piece
-// 2s + hh) at ((2j + s) * 64 + lane) * 16 bytes. The block T_01 = 0 is neither
-// written nor read; 6 KB of the 8 KB per chunk are used.
+// 2s + hh) at ((2j + s) * 64 + lane) * 16 bytes, 6 KB per chunk. The block
+// T_01 = 0 is neither written nor read.
 namespace tk {
 constexpr int WAVES = 4;                  // independent wavefronts per workgroup
-constexpr int CHUNK_ELEMS = 64 * 64;      // workspace elements per chunk
+constexpr int CHUNK_ELEMS = 3 * 32 * 32;  // workspace elements per chunk: T_00, T_11, T_10 (T_01 = 0)
 }  // namespace tk
 
 // Value of lane m of the caller's 16-lane row, in every lane of the row
@@ -359,7 +366,21 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     int L = p.lens ? ld_const(p.lens, b) : S;
     L = L < 0 ? 0 : (L > S ? S : L);
     const int t0 = c * C;
-    if (t0 >= L) return;
+    if (t0 >= L) {
+        // A chunk wholly past the length has no T. Its output rows are
+        // padding, written here as zeros (the pass over the chunks writes the
+        // rows of the chunks it processes): 64 rows of 256 bytes, rows past S
+        // dropped by the buffer bound.
+        const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<uint16_t *>(p.out) + ((size_t)b * Nv + h) * S * DV, (short)0, S * DV * 2, 0x00020000);
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int id = 64 * i + lane;
+            __builtin_amdgcn_raw_buffer_store_b128(z, ors, ((t0 + (id >> 4)) * DV + 8 * (id & 15)) * 2, 0, 0);
+        }
+        return;
+    }
 
     // K operands: row 32d + c32 of the chunk; k-step ks takes features
     // 16ks + 8hh .. + 7. The Gram blocks contract over the features, so any
@@ -557,37 +578,147 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
     for (int s = 0; s < 2; ++s) put(2, s, op8<EL>(T10, s));
 }
 
-// One workgroup per (sequence, value head, 64-column tile of Dv); the columns
-// of S evolve independently, so each tile carries its own slice of the state.
-// The chunk step is split so that only two products depend on the state:
+// The chunk step, split so that only two products depend on the state:
 //
 //   W = T diag(beta exp(gamma)) K,  U = T diag(beta) V,  T = (I + A)^-1
 //   Vnew = U - W S0
 //   O^T  = (S0^T Q^T) diag(exp(gamma)) + Vnew^T P^T          (scaled on store)
 //   S    = exp(gamma_C) S0 + K^T diag(exp(gamma_C - gamma)) Vnew
 //
-// Chain waves (6, 7) each own 32 state columns in float32 result registers
-// and, for chunk c, also form U = T diag(beta) V for their columns (it does
-// not depend on the state, so it fills gaps in the products' dependency
-// chains); their operands never leave registers except W, Q, P, K^T, V and
-// T diag(beta), read from the chunk's operand set.
-// Prep waves (0-5) build the operand set of chunk c + 1 meanwhile:
-//   stage K, Q and V in k-order and T as chunk_t_kernel wrote it;
-//   waves 0, 1, 4 form the three nonzero blocks of P, waves 0 and 1 then
-//   T diag(beta);
-//   waves 2, 3, 5 form W^T = K^T T'^T, T' = T diag(beta exp(gamma)), by 32
-//   features (wave 5 two blocks; waves 2 and 3 share their SIMDs with the
-//   chain waves).
+// The columns of S evolve independently, so a head's state may be split by
+// columns between workgroups. One workgroup per (sequence, value head, tile
+// of DV / NT columns): NT = 2 while there are too few heads to give every CU
+// a workgroup otherwise; NT = 1 (whole heads) once there are enough, so that
+// the state-independent work of a chunk is done once per head rather than
+// once per tile.
+//
+// Chain waves (the last DVT / 32) each own 32 state columns in float32 result
+// registers and, for chunk c, also form U for their columns (it does not
+// depend on the state, so it fills gaps in the products' dependency chains);
+// their operands never leave registers except W, Q, P, K^T, V and T, read
+// from the chunk's operand set.
+// Prep waves build the operand set of chunk c + 1 meanwhile.
+//   NT = 2, six prep waves: they stage K, Q and V in k-order and T as
+//   chunk_t_kernel wrote it; waves 0, 1, 4 form the three nonzero blocks of P,
+//   waves 0 and 1 then T diag(beta), U's left operand; waves 2, 3, 5 form -W
+//   by 32 features (wave 5 two blocks; waves 2 and 3 share their SIMDs with
+//   the chain waves).
+//   NT = 1, four prep waves, each sharing its SIMD with a chain wave: all four
+//   stage K, Q and the rows of diag(beta) V, so that T itself is U's left
+//   operand (T diag(beta) would not fit in LDS beside 128-column V tiles);
+//   wave 3 stages T and forms the per-token factors; waves 0-2 form the three
+//   blocks of P, and every wave one 32-feature block of -W.
 // Products that contract over tokens read K and V through LDS transpose
 // reads of the staged rows, so neither is ever transposed explicitly.
 // Chain and prep meet once per chunk at a workgroup barrier.
+
+// Rows 8m + 4hh + i (m, i = 0..3) of the 32-row block starting at r0 of a
+// per-token vector: the rows that a lane holds in a 32x32 result.
+__device__ __forceinline__ void lane_rows(const float *v, int r0, int hh, float *o)
+{
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const float4 x = *reinterpret_cast<const float4 *>(v + r0 + 8 * m + 4 * hh);
+        o[4 * m] = x.x; o[4 * m + 1] = x.y; o[4 * m + 2] = x.z; o[4 * m + 3] = x.w;
+    }
+}
+
+// P block (tokens r in 32-block rbq, keys i in 32-block ibq), written as rows
+// r: scale exp(gamma_r - gamma_i) q_r . k_i for i <= r, else 0. gv holds
+// gamma log2(e) per token.
+template <typename EL, bool ND>
+__device__ __forceinline__ void p_block(unsigned char *set, const float *gv, float scale, int rbq, int ibq, int lane)
+{
+    const int hh = lane >> 5, c32 = lane & 31;
+    f32x16_t G = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+        G = mfma32<EL>(ld8(set, mk::S_KT + sw256t(32 * ibq + c32, 2 * ks + hh)),
+                       ld8(set, mk::S_Q + sw256(32 * rbq + c32, 2 * ks + hh)), G);
+    const int r = 32 * rbq + c32;
+    if constexpr (ND) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) G[q] = 32 * ibq + drow(q, hh) <= r ? scale * G[q] : 0.f;
+    } else {
+        const float gq = gv[r];
+        float gi[16];
+        lane_rows(gv, 32 * ibq, hh, gi);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int i = 32 * ibq + drow(q, hh);
+            G[q] = i <= r ? scale * __builtin_amdgcn_exp2f(gq - gi[q]) * G[q] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) st8(set, mk::S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8<EL>(G, s));
+}
+
+// -W for the 32 features of block fbk, written as -W rows: -W^T = K^T (-T'^T)
+// with tp the six operands of -T' = -T diag(beta exp(gamma)).
+template <typename EL>
+__device__ __forceinline__ void w_block(unsigned char *set, const e16x8_t (&tp)[6], int fbk, int lane)
+{
+    const int hh = lane >> 5, c32 = lane & 31;
+    e16x8_t ak[4];
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ldT<256>(set + mk::S_KT, fbk, k2, lane);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        f32x16_t d = zero16();
+#pragma unroll
+        for (int k2 = 0; k2 < 2 * rb + 2; ++k2) d = mfma32<EL>(ak[k2], tp[rb == 0 ? k2 : 2 + k2], d);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) st8(set, mk::S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8<EL>(d, s));
+    }
+}
+
+// Per-token factors of a chunk (lane t = token t), from the raw beta (or its
+// logit) and g (or a) as loaded: gamma is the in-chunk cumulative log decay,
+// kept as gamma log2(e) for exp2. bg gets beta, gamma log2(e) and
+// beta exp(gamma); vec (in the operand set) the output, update and state
+// decays (nothing without decay: the chain then uses none).
+template <typename EL, bool FG, bool ND>
+__device__ __forceinline__ void token_factors(float *bg, float *vec, uint32_t rb, uint32_t rg, int nv, float scale,
+                                              float a_log, float dt_b, int lane)
+{
+    float beta = EL::to(rb);
+    if constexpr (ND) {
+        // Outputs need no per-row factor either: rows past the length have
+        // zero q.
+        bg[lane] = beta;
+        bg[64 + lane] = 0.f;
+        bg[128 + lane] = beta;
+    } else {
+        float g = __uint_as_float(rg);
+        if constexpr (FG) {
+            // Fused gates; tokens past the length are identity steps.
+            beta = lane < nv ? gate_sigmoid(beta) : 0.f;
+            g = lane < nv ? gate_g(EL::to(rg), a_log, dt_b) : 0.f;
+        }
+        const float gam2 = wave_prefix_sum(g) * 1.44269504088896340736f;
+        const float gamC2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam2), 63));
+        const float eg = __builtin_amdgcn_exp2f(gam2);
+        bg[lane] = beta;
+        bg[64 + lane] = gam2;
+        bg[128 + lane] = beta * eg;
+        vec[lane] = lane < nv ? scale * eg : 0.f;
+        vec[64 + lane] = __builtin_amdgcn_exp2f(gamC2 - gam2);
+        if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
+    }
+}
+
 // FG: fused gates (raw a and beta logits in place of g and beta).
 // ND: no decay (g absent, alpha = 1): every decay factor is 1, and the
 // multiplies by them are left out.
-template <typename EL, bool FG, bool ND>
+// NT: column tiles per head (1 or 2).
+template <typename EL, bool FG, bool ND, int NT>
 __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int units)
 {
     using namespace mk;
+    using TL = Tile<NT>;
+    constexpr int DVT = TL::DVT, NPREP = TL::NPREP, S_T = TL::S_T, S_VEC = TL::S_VEC, SET_BYTES = TL::SET_BYTES;
+    // U's left operand: T diag(beta) (NT = 2), or T with diag(beta) V staged (NT = 1).
+    constexpr int S_TU = NT == 2 ? TL::S_TB : TL::S_T;
     extern __shared__ __align__(16) unsigned char smem[];
 
     // Workgroup -> unit. Workgroups are dealt round-robin to the 8 XCDs, and
@@ -636,7 +767,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     const uint16_t *ib = p.init ? static_cast<const uint16_t *>(p.init) + ((size_t)b * Nv + h) * DK * DV + col0 : nullptr;
     uint16_t *fb = static_cast<uint16_t *>(p.fin) + ((size_t)b * Nv + h) * DK * DV + col0;
 
-    uint32_t *flags = reinterpret_cast<uint32_t *>(smem + P_FLAG);
+    uint32_t *flags = reinterpret_cast<uint32_t *>(smem + TL::P_FLAG);
     if (tid < 4) flags[tid] = 0u;
     lds_barrier();
 
@@ -680,7 +811,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
             {
                 e16x8_t bv[4];
 #pragma unroll
-                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<128>(set + S_VT, cw, k2, lane);
+                for (int k2 = 0; k2 < 4; ++k2) bv[k2] = ldT<2 * DVT>(set + S_VT, cw, k2, lane);
 #pragma unroll
                 for (int rb = 0; rb < 2; ++rb) {
                     ot[rb] = zero16();
@@ -688,7 +819,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
                     uu[rb] = zero16();
 #pragma unroll
                     for (int k2 = 0; k2 < 2 * rb + 2; ++k2)
-                        uu[rb] = mfma32<EL>(ld8(set + S_TB, t_operand_offset(rb == 0 ? k2 : 2 + k2, lane)), bv[k2], uu[rb]);
+                        uu[rb] = mfma32<EL>(ld8(set + S_TU, t_operand_offset(rb == 0 ? k2 : 2 + k2, lane)), bv[k2], uu[rb]);
                 }
             }
             {
@@ -799,225 +930,254 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         const int nchk = (S + C - 1) / C;
         const uint16_t *twb = static_cast<const uint16_t *>(p.work) + ((size_t)b * Nv + h) * nchk * tk::CHUNK_ELEMS;
         const __amdgpu_buffer_rsrc_t trs = __builtin_amdgcn_make_buffer_rsrc((void *)twb, (short)0, nchunks * tk::CHUNK_ELEMS * 2, 0x00020000);
-        // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
-        // waves 0-1 2 x 32 bytes of V and 3 x 16 bytes of T, wave 1 one beta
-        // and one g.
-        u32x4_t ra[8], rt[3], traw[3];
-        uint32_t rb = 0, rg = 0;
-        const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
-        auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
-            constexpr int W = decltype(R)::value;
-            const int t0 = cn * C;
-            if constexpr (W >= 2) {
+        float *bg = reinterpret_cast<float *>(smem + TL::P_BG);
+        const float *gv = bg + 64, *fv = bg + 128;
+
+        // K and Q rows of a chunk into k-ordered tiles: a row of 256 bytes spans
+        // 8 consecutive lanes, 32 bytes each; lane id of the 256 staging lanes.
+        auto stage_kq = [&](unsigned char *set, u32x4_t (&ra)[8], int id0) __attribute__((always_inline)) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
-                    const int off = ((t0 + row) * DK + 16 * grp) * 2;
-                    ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-                    ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
-                    ra[4 + 2 * m] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
-                    ra[5 + 2 * m] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0);
+            for (int m = 0; m < 2; ++m) {
+                const int id = id0 + 256 * m, row = id >> 3, grp = id & 7;
+                if (p.qk_norm) {
+                    u32x4_t kx[2] = {ra[2 * m], ra[2 * m + 1]}, qx[2] = {ra[4 + 2 * m], ra[5 + 2 * m]};
+                    normalise_row<EL, 8>(kx);
+                    normalise_row<EL, 8>(qx);
+                    ra[2 * m] = kx[0]; ra[2 * m + 1] = kx[1];
+                    ra[4 + 2 * m] = qx[0]; ra[5 + 2 * m] = qx[1];
                 }
-            } else {
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
-                    const int off = ((t0 + row) * DV + 16 * grp) * 2;
-                    ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
-                    ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16, 0, 0);
-                }
-#pragma unroll
-                for (int n = 0; n < 3; ++n)
-                    rt[n] = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + (ltid + 128 * n) * 16, 0, 0);
-                if constexpr (W == 1) {
-                    rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
-                    if constexpr (!ND)
-                        rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
-                                : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
-                }
+                *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp)) = korder_lo(ra[4 + 2 * m], ra[5 + 2 * m]);
+                *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp + 1)) = korder_hi(ra[4 + 2 * m], ra[5 + 2 * m]);
             }
         };
-        float *bg = reinterpret_cast<float *>(smem + P_BG);
-
-        auto prep = [&](auto R, int cn) __attribute__((always_inline)) {
-            constexpr int W = decltype(R)::value;
-            unsigned char *set = smem + (cn & 1) * SET_BYTES;
-            const uint32_t ncall = (uint32_t)cn + 1u;
-
-            // ---- stage chunk cn (K rows into the W slot, V rows into the U slot) ----
-            if constexpr (W >= 2) {
+        auto issue_kq = [&](u32x4_t (&ra)[8], int id0, int t0) __attribute__((always_inline)) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int id = ltid + 256 * m, row = id >> 3, grp = id & 7;
-                    if (p.qk_norm) {
-                        // A row of K or Q spans 8 consecutive lanes, 32 bytes each.
-                        u32x4_t kx[2] = {ra[2 * m], ra[2 * m + 1]}, qx[2] = {ra[4 + 2 * m], ra[5 + 2 * m]};
-                        normalise_row<EL, 8>(kx);
-                        normalise_row<EL, 8>(qx);
-                        ra[2 * m] = kx[0]; ra[2 * m + 1] = kx[1];
-                        ra[4 + 2 * m] = qx[0]; ra[5 + 2 * m] = qx[1];
-                    }
-                    *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
-                    *reinterpret_cast<u32x4_t *>(set + S_KT + sw256t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
-                    *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp)) = korder_lo(ra[4 + 2 * m], ra[5 + 2 * m]);
-                    *reinterpret_cast<u32x4_t *>(set + S_Q + sw256(row, 2 * grp + 1)) = korder_hi(ra[4 + 2 * m], ra[5 + 2 * m]);
-                }
-            } else {
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
-                    *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
-                    *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
-                }
-#pragma unroll
-                for (int n = 0; n < 3; ++n) {
-                    *reinterpret_cast<u32x4_t *>(set + S_T + (ltid + 128 * n) * 16) = rt[n];
-                    traw[n] = rt[n];
-                }
-                if constexpr (W == 1 && ND) {
-                    // No decay: beta alone. The outputs need no per-row factor,
-                    // since rows past the length have zero q.
-                    const float beta = EL::to(rb);
-                    bg[lane] = beta;
-                    bg[64 + lane] = 0.f;
-                    bg[128 + lane] = beta;
-                } else if constexpr (W == 1) {
-                    // Per-token factors of chunk cn (lane t = token t): gamma is the
-                    // in-chunk cumulative log decay, kept as gamma log2(e) for exp2.
-                    const int nv = min(C, L - cn * C);
-                    float beta = EL::to(rb), g = __uint_as_float(rg);
-                    if (fg) {
-                        // Fused gates; tokens past the length are identity steps.
-                        beta = lane < nv ? gate_sigmoid(beta) : 0.f;
-                        g = lane < nv ? gate_g(EL::to(rg), a_log, dt_b) : 0.f;
-                    }
-                    const float gam2 = wave_prefix_sum(g) * 1.44269504088896340736f;
-                    const float gamC2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gam2), 63));
-                    const float eg = __builtin_amdgcn_exp2f(gam2);
-                    bg[lane] = beta;
-                    bg[64 + lane] = gam2;
-                    bg[128 + lane] = beta * eg;
-                    float *vec = reinterpret_cast<float *>(set + S_VEC);
-                    vec[lane] = lane < nv ? p.scale * eg : 0.f;
-                    vec[64 + lane] = __builtin_amdgcn_exp2f(gamC2 - gam2);
-                    if (lane == 0) vec[128] = __builtin_amdgcn_exp2f(gamC2);
-                }
+            for (int m = 0; m < 2; ++m) {
+                const int id = id0 + 256 * m, row = id >> 3, grp = id & 7;
+                const int off = ((t0 + row) * DK + 16 * grp) * 2;
+                ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+                ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(krs, off + 16, 0, 0);
+                ra[4 + 2 * m] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+                ra[5 + 2 * m] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off + 16, 0, 0);
             }
-            issue(R, cn + 1);
-            arrive(flags + 0, lane);
-            wait_for(flags + 0, 6u * ncall);
+        };
+        auto issue_factors = [&](uint32_t &rb, uint32_t &rg, int t0) __attribute__((always_inline)) {
+            rb = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + lane) * 2, 0, 0);
+            if constexpr (!ND)
+                rg = fg ? __builtin_amdgcn_raw_buffer_load_b16(grs, (t0 + lane) * 2, 0, 0)
+                        : __builtin_amdgcn_raw_buffer_load_b32(grs, (t0 + lane) * 4, 0, 0);
+        };
 
-            // beta, gamma log2(e) and beta exp(gamma) of the rows a lane holds in
-            // a result tile: rows 8m + 4hh + i of the 32-row block starting at r0.
-            const float *gv = bg + 64, *fv = bg + 128;
-            auto rows4 = [&](const float *v, int r0, float *o) __attribute__((always_inline)) {
+        if constexpr (NT == 2) {
+            // Chunk inputs in flight: waves 2-5 hold 2 x 32 bytes of K and of Q,
+            // waves 0-1 2 x 32 bytes of V and 3 x 16 bytes of T, wave 1 one beta
+            // and one g.
+            u32x4_t ra[8], rt[3], traw[3];
+            uint32_t rb = 0, rg = 0;
+            const int ltid = wv >= 2 ? tid - 128 : tid;   // 0-255 for K/Q, 0-127 for V
+            auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
+                constexpr int W = decltype(R)::value;
+                const int t0 = cn * C;
+                if constexpr (W >= 2) {
+                    issue_kq(ra, ltid, t0);
+                } else {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const float4 x = *reinterpret_cast<const float4 *>(v + r0 + 8 * m + 4 * hh);
-                    o[4 * m] = x.x; o[4 * m + 1] = x.y; o[4 * m + 2] = x.z; o[4 * m + 3] = x.w;
+                    for (int m = 0; m < 2; ++m) {
+                        const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
+                        const int off = ((t0 + row) * DV + 16 * grp) * 2;
+                        ra[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+                        ra[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16, 0, 0);
+                    }
+#pragma unroll
+                    for (int n = 0; n < 3; ++n)
+                        rt[n] = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + (ltid + 128 * n) * 16, 0, 0);
+                    if constexpr (W == 1) issue_factors(rb, rg, t0);
                 }
             };
 
-            if constexpr (W == 0 || W == 1 || W == 4) {
-                // P block (tokens r in block rbq, keys i in block ibq), written as rows r.
-                constexpr int rbq = W == 0 ? 0 : 1, ibq = W == 4 ? 1 : 0;
-                f32x16_t G = zero16();
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-                    G = mfma32<EL>(ld8(set, S_KT + sw256t(32 * ibq + c32, 2 * ks + hh)),
-                               ld8(set, S_Q + sw256(32 * rbq + c32, 2 * ks + hh)), G);
-                const int r = 32 * rbq + c32;
-                if constexpr (ND) {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) G[q] = 32 * ibq + drow(q, hh) <= r ? p.scale * G[q] : 0.f;
+            auto prep = [&](auto R, int cn) __attribute__((always_inline)) {
+                constexpr int W = decltype(R)::value;
+                unsigned char *set = smem + (cn & 1) * SET_BYTES;
+                const uint32_t ncall = (uint32_t)cn + 1u;
+
+                // ---- stage chunk cn (K and Q rows, V rows, T) ----
+                if constexpr (W >= 2) {
+                    stage_kq(set, ra, ltid);
                 } else {
-                    const float gq = gv[r];
-                    float gi[16];
-                    rows4(gv, 32 * ibq, gi);
 #pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int i = 32 * ibq + drow(q, hh);
-                        G[q] = i <= r ? p.scale * __builtin_amdgcn_exp2f(gq - gi[q]) * G[q] : 0.f;
+                    for (int m = 0; m < 2; ++m) {
+                        const int id = ltid + 128 * m, row = id >> 2, grp = id & 3;
+                        *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp)) = korder_lo(ra[2 * m], ra[2 * m + 1]);
+                        *reinterpret_cast<u32x4_t *>(set + S_VT + sw128t(row, 2 * grp + 1)) = korder_hi(ra[2 * m], ra[2 * m + 1]);
+                    }
+#pragma unroll
+                    for (int n = 0; n < 3; ++n) {
+                        *reinterpret_cast<u32x4_t *>(set + S_T + (ltid + 128 * n) * 16) = rt[n];
+                        traw[n] = rt[n];
+                    }
+                    if constexpr (W == 1)
+                        token_factors<EL, FG, ND>(bg, reinterpret_cast<float *>(set + S_VEC), rb, rg, min(C, L - cn * C),
+                                                  p.scale, a_log, dt_b, lane);
+                }
+                issue(R, cn + 1);
+                arrive(flags + 0, lane);
+                wait_for(flags + 0, 6u * ncall);
+
+                if constexpr (W == 0 || W == 1 || W == 4)
+                    p_block<EL, ND>(set, gv, p.scale, W == 0 ? 0 : 1, W == 4 ? 1 : 0, lane);
+                if constexpr (W < 2) {
+                    // T diag(beta) for the chain's U, from this lane's three pieces
+                    // of T (block j = n, k-step s = W: tokens 16 k2 + 4hh + {0..3,
+                    // 8..11} with k2 = s, or 2 + s in T_11).
+#pragma unroll
+                    for (int n = 0; n < 3; ++n) {
+                        const int i0 = 16 * (n == 1 ? 2 + W : W) + 4 * hh;
+                        const float4 f0 = *reinterpret_cast<const float4 *>(bg + i0), f1 = *reinterpret_cast<const float4 *>(bg + i0 + 8);
+                        const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                        const uint32_t w4[4] = {traw[n].x, traw[n].y, traw[n].z, traw[n].w};
+                        float r[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) r[e] = ((e & 1) ? EL::hi(w4[e >> 1]) : EL::lo(w4[e >> 1])) * fe[e];
+                        st8(set, TL::S_TB + (ltid + 128 * n) * 16, pack8<EL>(r));
                     }
                 }
+                if constexpr (W == 2 || W == 3 || W == 5) {
+                    // -W by 32 features: blocks 2 and 3 on waves 2 and 3, blocks
+                    // 0 and 1 on wave 5.
+                    e16x8_t tp[6];
 #pragma unroll
-                for (int s = 0; s < 2; ++s) st8(set, S_P + sw128(r, 2 * (2 * ibq + s) + hh), op8<EL>(G, s));
-            }
-            if constexpr (W < 2) {
-                // T diag(beta) for the chain's U, from this lane's three pieces
-                // of T (block j = n, k-step s = W: tokens 16 k2 + 4hh + {0..3,
-                // 8..11} with k2 = s, or 2 + s in T_11).
-#pragma unroll
-                for (int n = 0; n < 3; ++n) {
-                    const int i0 = 16 * (n == 1 ? 2 + W : W) + 4 * hh;
-                    const float4 f0 = *reinterpret_cast<const float4 *>(bg + i0), f1 = *reinterpret_cast<const float4 *>(bg + i0 + 8);
-                    const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                    const uint32_t w4[4] = {traw[n].x, traw[n].y, traw[n].z, traw[n].w};
-                    float r[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) r[e] = ((e & 1) ? EL::hi(w4[e >> 1]) : EL::lo(w4[e >> 1])) * fe[e];
-                    st8(set, S_TB + (ltid + 128 * n) * 16, pack8<EL>(r));
+                    for (int n = 0; n < 6; ++n) tp[n] = t_operand<EL, true>(set + S_T, n, fv, lane);
+                    if constexpr (W == 5) {
+                        w_block<EL>(set, tp, 0, lane);
+                        w_block<EL>(set, tp, 1, lane);
+                    } else {
+                        w_block<EL>(set, tp, W, lane);
+                    }
                 }
+            };
+
+            // Each role runs its own copy of the loop, so that it keeps only its
+            // own addresses and values live.
+            auto run = [&](auto R) __attribute__((always_inline)) {
+                if (nchunks > 0) {
+                    issue(R, 0);
+                    prep(R, 0);
+                    lds_barrier();
+                    for (int c = 0; c + 1 < nchunks; ++c) {
+                        prep(R, c + 1);
+                        lds_barrier();
+                    }
+                    lds_barrier();   // the chain's last chunk
+                }
+            };
+            switch (wv) {
+            case 0: run(std::integral_constant<int, 0>{}); break;
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            case 4: run(std::integral_constant<int, 4>{}); break;
+            default: run(std::integral_constant<int, 5>{}); break;
             }
-            if constexpr (W == 2 || W == 3 || W == 5) {
-                // -W^T = -(K^T T'^T), T' = T diag(beta exp(gamma)), by 32
-                // features, written as -W rows: feature blocks 2 and 3 on waves
-                // 2 and 3, blocks 0 and 1 on wave 5.
+        } else {
+            // Whole rows, four prep waves. Chunk inputs in flight: every lane
+            // holds 2 x 32 bytes each of K, Q and V and the betas of its two V
+            // rows; waves 0-2 also two 16-byte pieces of T, wave 3 one beta
+            // and one g for the per-token factors. The K, Q and V loads of the
+            // next chunk are issued as soon as these are staged, ahead of the
+            // smaller jobs, so that they have a whole chunk period to land.
+            u32x4_t ra[8], rv[4], rt[2];
+            uint32_t rbv[2] = {0u, 0u}, rb = 0, rg = 0;
+            auto issue_rows = [&](int cn) __attribute__((always_inline)) {
+                const int t0 = cn * C;
+                issue_kq(ra, tid, t0);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int id = tid + 256 * m, row = id >> 3, grp = id & 7;
+                    const int off = ((t0 + row) * DV + 16 * grp) * 2;
+                    rv[2 * m] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+                    rv[2 * m + 1] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + 16, 0, 0);
+                    rbv[m] = __builtin_amdgcn_raw_buffer_load_b16(brs, (t0 + row) * 2, 0, 0);
+                }
+            };
+            auto issue_aux = [&](auto R, int cn) __attribute__((always_inline)) {
+                constexpr int W = decltype(R)::value;
+                if constexpr (W < 3) {
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        rt[n] = __builtin_amdgcn_raw_buffer_load_b128(trs, cn * tk::CHUNK_ELEMS * 2 + (tid + 192 * n) * 16, 0, 0);
+                } else {
+                    issue_factors(rb, rg, cn * C);
+                }
+            };
+            auto issue = [&](auto R, int cn) __attribute__((always_inline)) {
+                issue_rows(cn);
+                issue_aux(R, cn);
+            };
+
+            auto prep = [&](auto R, int cn) __attribute__((always_inline)) {
+                constexpr int W = decltype(R)::value;
+                unsigned char *set = smem + (cn & 1) * SET_BYTES;
+                const uint32_t ncall = (uint32_t)cn + 1u;
+
+                // ---- stage chunk cn (K and Q rows, diag(beta) V rows, T) ----
+                stage_kq(set, ra, tid);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    // Rows past the length are zero whatever their beta.
+                    const int id = tid + 256 * m, row = id >> 3, grp = id & 7;
+                    float bt = EL::to(rbv[m]);
+                    if constexpr (FG) bt = gate_sigmoid(bt);
+                    uint32_t w[8] = {rv[2 * m].x, rv[2 * m].y, rv[2 * m].z, rv[2 * m].w,
+                                     rv[2 * m + 1].x, rv[2 * m + 1].y, rv[2 * m + 1].z, rv[2 * m + 1].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = EL::pack(EL::lo(w[e]) * bt, EL::hi(w[e]) * bt);
+                    const u32x4_t a = {w[0], w[1], w[2], w[3]}, c = {w[4], w[5], w[6], w[7]};
+                    *reinterpret_cast<u32x4_t *>(set + S_VT + sw256t(row, 2 * grp)) = korder_lo(a, c);
+                    *reinterpret_cast<u32x4_t *>(set + S_VT + sw256t(row, 2 * grp + 1)) = korder_hi(a, c);
+                }
+                issue_rows(cn + 1);
+                if constexpr (W < 3) {
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) *reinterpret_cast<u32x4_t *>(set + S_T + (tid + 192 * n) * 16) = rt[n];
+                } else {
+                    token_factors<EL, FG, ND>(bg, reinterpret_cast<float *>(set + S_VEC), rb, rg, min(C, L - cn * C),
+                                              p.scale, a_log, dt_b, lane);
+                }
+                issue_aux(R, cn + 1);
+                arrive(flags + 0, lane);
+                wait_for(flags + 0, 4u * ncall);
+
+                if constexpr (W < 3) p_block<EL, ND>(set, gv, p.scale, W == 0 ? 0 : 1, W == 2 ? 1 : 0, lane);
                 e16x8_t tp[6];
 #pragma unroll
                 for (int n = 0; n < 6; ++n) tp[n] = t_operand<EL, true>(set + S_T, n, fv, lane);
-                auto wblock = [&](int fbk) __attribute__((always_inline)) {
-                    e16x8_t ak[4];
-#pragma unroll
-                    for (int k2 = 0; k2 < 4; ++k2) ak[k2] = ldT<256>(set + S_KT, fbk, k2, lane);
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        f32x16_t d = zero16();
-#pragma unroll
-                        for (int k2 = 0; k2 < 2 * rb + 2; ++k2) d = mfma32<EL>(ak[k2], tp[rb == 0 ? k2 : 2 + k2], d);
-#pragma unroll
-                        for (int s = 0; s < 2; ++s) st8(set, S_W + sw256(32 * rb + c32, 2 * (2 * fbk + s) + hh), op8<EL>(d, s));
-                    }
-                };
-                if constexpr (W == 5) {
-                    wblock(0);
-                    wblock(1);
-                } else {
-                    wblock(W);
-                }
-            }
-        };
+                w_block<EL>(set, tp, W, lane);
+            };
 
-        // Each role runs its own copy of the loop, so that it keeps only its
-        // own addresses and values live.
-        auto run = [&](auto R) __attribute__((always_inline)) {
-            if (nchunks > 0) {
-                issue(R, 0);
-                prep(R, 0);
-                lds_barrier();
-                for (int c = 0; c + 1 < nchunks; ++c) {
-                    prep(R, c + 1);
+            auto run = [&](auto R) __attribute__((always_inline)) {
+                if (nchunks > 0) {
+                    issue(R, 0);
+                    prep(R, 0);
                     lds_barrier();
+                    for (int c = 0; c + 1 < nchunks; ++c) {
+                        prep(R, c + 1);
+                        lds_barrier();
+                    }
+                    lds_barrier();   // the chain's last chunk
                 }
-                lds_barrier();   // the chain's last chunk
+            };
+            switch (wv) {
+            case 0: run(std::integral_constant<int, 0>{}); break;
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            default: run(std::integral_constant<int, 3>{}); break;
             }
-        };
-        switch (wv) {
-        case 0: run(std::integral_constant<int, 0>{}); break;
-        case 1: run(std::integral_constant<int, 1>{}); break;
-        case 2: run(std::integral_constant<int, 2>{}); break;
-        case 3: run(std::integral_constant<int, 3>{}); break;
-        case 4: run(std::integral_constant<int, 4>{}); break;
-        default: run(std::integral_constant<int, 5>{}); break;
         }
     }
-
-    // Zeros for every output row past the last processed chunk.
-    const int tz = nchunks * C;
-    for (int id = tid; id < (S - tz) * (DVT / 8); id += NTHR) {
-        const int row = tz + id / (DVT / 8), cv = (id % (DVT / 8)) * 8;
-        *reinterpret_cast<uint4 *>(ob + (size_t)row * DV + cv) = make_uint4(0, 0, 0, 0);
-    }
+    // Output rows of the chunks past the last one processed are padding,
+    // zeroed by chunk_t_kernel.
 }
 
 // ---------------------------------------------------------------------------
@@ -1150,6 +1310,18 @@ int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, i
     return 0;
 }
 
+// The matrix-core kernel for an element format (0 bf16, 1 fp16), a form (0
+// plain, 1 fused gates, 2 no decay) and NT column tiles per head.
+static const void *mfma_variant(int half, int form, int nt)
+{
+#define GDR_MFMA_FORMS(EL_, NT_)                                                                                 \
+    (form == 1 ? (const void *)chunk_mfma_kernel<EL_, true, false, NT_>                                          \
+               : (form == 2 ? (const void *)chunk_mfma_kernel<EL_, false, true, NT_> : (const void *)chunk_mfma_kernel<EL_, false, false, NT_>))
+    if (half) return nt == 1 ? GDR_MFMA_FORMS(F16, 1) : GDR_MFMA_FORMS(F16, 2);
+    return nt == 1 ? GDR_MFMA_FORMS(BF16, 1) : GDR_MFMA_FORMS(BF16, 2);
+#undef GDR_MFMA_FORMS
+}
+
 hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, hipStream_t s, bool *supported)
 {
     *supported = true;
@@ -1167,8 +1339,11 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
                                                      targs, 0, s);
                 if (e != hipSuccess) return e;
             }
-            const int units = p.B * p.Nv * mk::NT;
-            const int G = mk::NT * (p.Nv / p.Nk);   // units of one (b, key head), kept on one XCD
+            // Whole heads per workgroup once there are enough heads, else
+            // column halves.
+            const int nt = (int64_t)p.B * p.Nv >= mk::WHOLE_ROW_HEADS ? 1 : 2;
+            const int units = p.B * p.Nv * nt;
+            const int G = nt * (p.Nv / p.Nk);   // units of one (b, key head), kept on one XCD
             const int nwg = (units + 8 * G - 1) / (8 * G) * (8 * G);
             int u = units;
             void *args[] = {&pc, &u};
@@ -1181,20 +1356,17 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
             if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
             const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
             if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
-                for (const void *f : {(const void *)chunk_mfma_kernel<BF16, false, false>, (const void *)chunk_mfma_kernel<BF16, true, false>,
-                                      (const void *)chunk_mfma_kernel<BF16, false, true>, (const void *)chunk_mfma_kernel<F16, false, false>,
-                                      (const void *)chunk_mfma_kernel<F16, true, false>, (const void *)chunk_mfma_kernel<F16, false, true>}) {
-                    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, mk::LDS_BYTES);
+                for (int t = 0; t < 12; ++t) {
+                    hipError_t e = hipFuncSetAttribute(mfma_variant(t & 1, (t >> 1) % 3, t < 6 ? 1 : 2),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, t < 6 ? mk::Tile<1>::LDS_BYTES
+                                                                                                        : mk::Tile<2>::LDS_BYTES);
                     if (e != hipSuccess) return e;
                 }
                 attr_done.fetch_or(bit, std::memory_order_acq_rel);
             }
-            const bool nd = !pc.gate_a && !pc.g;
-            const void *fn = half ? (pc.gate_a ? (const void *)chunk_mfma_kernel<F16, true, false>
-                                               : (nd ? (const void *)chunk_mfma_kernel<F16, false, true> : (const void *)chunk_mfma_kernel<F16, false, false>))
-                                  : (pc.gate_a ? (const void *)chunk_mfma_kernel<BF16, true, false>
-                                               : (nd ? (const void *)chunk_mfma_kernel<BF16, false, true> : (const void *)chunk_mfma_kernel<BF16, false, false>));
-            return hipLaunchKernel(fn, dim3(nwg), dim3(mk::NTHR), args, mk::LDS_BYTES, s);
+            const int form = pc.gate_a ? 1 : (!pc.g ? 2 : 0);
+            return hipLaunchKernel(mfma_variant(half, form, nt), dim3(nwg), dim3(mk::NTHR), args,
+                                   nt == 1 ? mk::Tile<1>::LDS_BYTES : mk::Tile<2>::LDS_BYTES, s);
         }
         *supported = false;
         return hipSuccess;

@@ -195,7 +195,7 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  * is carried in float32 between chunks.
  * Supported: bf16 or fp16 with Dk = Dv = 128 and chunk_size 64 (matrix-core
  *   path, which first forms (I + A)^-1 of every chunk in the workspace:
- *   B * Nv * ceil(S / 64) * 8192 bytes); f32 with Dk = Dv in {16, 32} and
+ *   B * Nv * ceil(S / 64) * 6144 bytes); f32 with Dk = Dv in {16, 32} and
  *   chunk_size in {16, 32, 64}, or Dk = Dv = 64 and chunk_size in {16, 32}
  *   (no workspace).
  * Errors: GDR_ERR_NULL if a, q, k, v, out or final_state is NULL, beta is
@@ -326,7 +326,7 @@ GDR_API gdr_status gdr_conv_decode(const gdr_conv_decode_args *a, void *stream);
  *   GDR_ERR_SCRATCH_LIMIT beyond the limit (nothing is enqueued), and
  *   GDR_ERR_LAUNCH if the array's address cannot be resolved.
  */
-#define GDR_NOALLOC_SCRATCH_BYTES (64LL << 20)
+#define GDR_NOALLOC_SCRATCH_BYTES (48LL << 20)
 GDR_API gdr_status gdr_chunk_noalloc(const gdr_chunk_args *a, void *stream);
 
 /* Bytes of workspace gdr_chunk needs for these arguments (0 if none; reads
@@ -339,7 +339,7 @@ GDR_API const char *gdr_status_string(gdr_status s);
 /* ABI version of this header (incremented on any layout change). */
 GDR_API int32_t gdr_abi_version(void);
 
-#define GDR_ABI_VERSION 7
+#define GDR_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

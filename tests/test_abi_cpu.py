@@ -154,7 +154,7 @@ def test_decode_validation(lib, kw, code):
     (dict(dtype=gdr.GDR_F32, Dk=64, Dv=64, chunk_size=64), gdr.GDR_ERR_UNSUPPORTED),
     (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
     (dict(workspace=None), gdr.GDR_ERR_NULL),
-    (dict(workspace_bytes=2 * 4 * 2 * 8192 - 1), gdr.GDR_ERR_SHAPE),
+    (dict(workspace_bytes=2 * 4 * 2 * 6144 - 1), gdr.GDR_ERR_SHAPE),
     (dict(workspace=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
     (dict(S=1 << 23), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, q=None, out=None, workspace=None), gdr.GDR_OK),
@@ -171,7 +171,7 @@ def test_chunk_validation(lib, kw, code):
 
 # The allocation-free entry point validates like gdr_chunk, ignores the
 # workspace fields, and refuses calls whose scratch exceeds its fixed array
-# (B * Nv * ceil(S / 64) chunks of 8 KiB on the bf16 path) before touching
+# (B * Nv * ceil(S / 64) chunks of 6 KiB on the bf16 path) before touching
 # the device. Calls that pass validation are GPU tests.
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=-1), gdr.GDR_ERR_DTYPE),
@@ -286,9 +286,9 @@ def test_binding_maps_status_to_exceptions(lib):
 def test_chunk_workspace_size(lib):
     # The matrix-core path needs 8 KB per (sequence, value head, chunk of 64);
     # the float32 path needs none.
-    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk())) == 2 * 4 * 2 * 8192
-    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=128))) == 2 * 4 * 2 * 8192
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk())) == 2 * 4 * 2 * 6144
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=128))) == 2 * 4 * 2 * 6144
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=0))) == 0
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F32, Dk=32, Dv=32, chunk_size=32))) == 0
-    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F16))) == 2 * 4 * 2 * 8192
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F16))) == 2 * 4 * 2 * 6144
     assert lib.gdr_chunk_workspace_size(None) == -1

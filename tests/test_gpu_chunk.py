@@ -70,6 +70,50 @@ def test_varlen_no_decay_full():
     check_all_units(c, out, fin, "varlen prefill workload")
 
 
+# --- workgroups of whole heads (from 512 (b, h) heads on) -------------------
+# The launch takes one workgroup per whole head once B * Nv reaches 512, and a
+# workgroup per half of the value columns below that; the workloads above
+# cover B * Nv = 128 (halves) and 1024 (whole heads).
+
+@pytest.mark.parametrize("gate", ["g", None], ids=["decay", "no-decay"])
+def test_whole_heads(gate):
+    # several chunks, ragged, one-token and empty sequences, an initial state;
+    # NaN in every padded input position
+    kw = dict(B=8, Nk=16, Nv=64, S=200, lens=[200, 129, 64, 1, 0, 150, 77, 200], poison_pad=True)
+    c = synth.config(4, base=431, **kw) if gate else synth.config(5, base=432, init_std=0.02, **kw)
+    assert c.B * c.Nv >= 512
+    out, fin = run_chunk(c)
+    assert bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(fin.float()).all())
+    _check_full(c, out, fin)
+
+
+@pytest.mark.parametrize("gate", [None, "gate"])
+@pytest.mark.parametrize("mix", [0.9, 1.0, ("vocab", 4)], ids=str)
+def test_whole_heads_correlated_keys(mix, gate):
+    c = synth.prefill_case(B=4, Nk=8, Nv=128, S=130, Dk=128, Dv=128, base=433, gate=gate, key_mix=mix,
+                           lens=[130, 64, 1, 99], init_std=0.02)
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
+def test_whole_heads_agree_with_column_halves():
+    # the same heads through both launches (a 256-head half of the batch takes
+    # the column halves). They round differently in one place (diag(beta)
+    # joins T or V before its bf16 rounding), so they agree to the parity bar,
+    # and both are checked against the oracle.
+    c = synth.config(4, B=8, Nk=16, Nv=64, S=130, lens=[130, 64, 1, 0, 99, 130, 128, 65], base=434)
+    o_all, f_all = run_chunk(c)
+    h = synth.config(4, B=4, Nk=16, Nv=64, S=130, lens=[130, 64, 1, 0], base=434)
+    assert h.B * h.Nv < 512 and np.array_equal(h.q, c.q[:4]) and np.array_equal(h.v, c.v[:4])
+    o_half, f_half = run_chunk(h)
+    _check_full(h, o_half, f_half)
+    eo = max_err(to_f64(o_all[:4]), to_f64(o_half))
+    ef = max_err(to_f64(f_all[:4]), to_f64(f_half))
+    say(f"whole heads vs column halves: output {eo:.3e}, final state {ef:.3e}")
+    assert eo <= TOL[c.dtype] and ef <= TOL[c.dtype]
+    assert_zero_rows(o_all, c.valid_lengths())
+
+
 def test_nan_in_padding_is_never_read():
     c = synth.config(4, B=3, Nk=1, Nv=2, S=200, lens=[200, 130, 1], base=416, poison_pad=True)
     out, fin = run_chunk(c)

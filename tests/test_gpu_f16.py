@@ -65,6 +65,13 @@ def test_f16_prefill_reduced():
     _check_full(c, out, fin)
 
 
+def test_f16_whole_heads():
+    # 512 heads: one workgroup per whole head
+    c = synth.config(4, B=8, Nk=16, Nv=64, S=200, lens=[200, 129, 64, 1, 0, 150, 77, 200], base=911, **F16)
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
 def test_f16_prefill_workload_full():
     c = synth.config(4, **F16)
     out, fin = run_chunk(c)

@@ -142,3 +142,10 @@ def test_qk_norm_prefill_no_decay():
     # length must still come out zero with normalised (zero) q rows there
     c = synth.config(5, B=3, Nk=2, Nv=4, S=300, lens=[300, 129, 1], base=626)
     _chunk(c, 626, gates=False, qk_norm=True)
+
+
+def test_whole_heads_fused_gates_and_qk_norm():
+    # 512 heads: one workgroup per whole head, which scales the staged V rows
+    # by the gate's beta; NaN gate inputs in the padding must never be read
+    c = synth.config(4, B=8, Nk=16, Nv=64, S=130, lens=[130, 64, 1, 0, 99, 130, 128, 65], base=627, poison_pad=True)
+    _chunk(c, 627, poison=True, gates=True, qk_norm=True)
