@@ -182,9 +182,6 @@ constexpr int C = 64;          // chunk length
 constexpr int DK = 128;        // key head size
 constexpr int DV = 128;        // value head size
 constexpr int NTHR = 512;      // 8 wavefronts: prep waves, then chain waves
-// Heads from which a workgroup takes a whole head (NT = 1) rather than half
-// of its value columns (NT = 2): two per CU of a 256-CU chip.
-constexpr int WHOLE_ROW_HEADS = 512;
 // Operand set of one chunk (double-buffered: the chain consumes chunk c while
 // the prep waves build chunk c + 1). Byte offsets within a set:
 constexpr int S_Q = 0;         // Q rows, features in k-order             [64][256 B]
@@ -587,10 +584,10 @@ __global__ __launch_bounds__(64 * tk::WAVES) __attribute__((amdgpu_waves_per_eu(
 //
 // The columns of S evolve independently, so a head's state may be split by
 // columns between workgroups. One workgroup per (sequence, value head, tile
-// of DV / NT columns): NT = 2 while there are too few heads to give every CU
-// a workgroup otherwise; NT = 1 (whole heads) once there are enough, so that
-// the state-independent work of a chunk is done once per head rather than
-// once per tile.
+// of DV / NT columns): NT = 2 while the column halves of all heads fit one
+// workgroup per CU; NT = 1 (whole heads) beyond that, so that the
+// state-independent work of a chunk is done once per head rather than once
+// per tile.
 //
 // Chain waves (the last DVT / 32) each own 32 state columns in float32 result
 // registers and, for chunk c, also form U for their columns (it does not
@@ -774,9 +771,13 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
     if (wv >= NPREP) {
         // ------------------------------ chain ------------------------------
         const int cw = wv - NPREP;   // state columns [32cw, 32cw + 32) of the tile
-        // The recurrence is the critical path: its instructions win issue
-        // arbitration against the prep waves sharing the SIMD.
-        __builtin_amdgcn_s_setprio(2);
+        // With column halves the recurrence is the critical path: its
+        // instructions win issue arbitration against the prep waves sharing
+        // the SIMD. With whole heads every SIMD holds a chain wave and a prep
+        // wave, the prep's path is the longer one, and equal priority measured
+        // best (varlen prefill pass 1330 us, against 1411 with the chain
+        // raised by one and 1429 by two).
+        if constexpr (NT == 2) __builtin_amdgcn_s_setprio(2);
         // Outputs go through a buffer resource bounded by this head's output
         // plane: stores of rows past S fall outside it and are dropped by the
         // hardware bounds check, with no branch in the loop.
@@ -1339,9 +1340,16 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
                                                      targs, 0, s);
                 if (e != hipSuccess) return e;
             }
-            // Whole heads per workgroup once there are enough heads, else
-            // column halves.
-            const int nt = (int64_t)p.B * p.Nv >= mk::WHOLE_ROW_HEADS ? 1 : 2;
+            int dev = 0;
+            if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+            // Column halves (NT = 2) while they fit one workgroup per CU, else
+            // whole heads (NT = 1): a whole-head workgroup takes about 1.7x as
+            // long per chunk as a half-head one, but does the work of two
+            // (measured: 187.6 against 213.2 us at 128 heads of 4096 tokens,
+            // 292.4 against 231.2 us at 160, 718.8 against 581.5 us at 512).
+            int ncu = 0;
+            if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+            const int nt = 2LL * p.B * p.Nv > ncu ? 1 : 2;
             const int units = p.B * p.Nv * nt;
             const int G = nt * (p.Nv / p.Nk);   // units of one (b, key head), kept on one XCD
             const int nwg = (units + 8 * G - 1) / (8 * G) * (8 * G);
@@ -1352,8 +1360,6 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
             // set after the attribute is in place; racing first calls both
             // set it, which is harmless.
             static std::atomic<uint64_t> attr_done{0};
-            int dev = 0;
-            if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
             const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
             if (!bit || !(attr_done.load(std::memory_order_acquire) & bit)) {
                 for (int t = 0; t < 12; ++t) {
