@@ -169,6 +169,12 @@ def test_epilogue_prefill():
     _chunk(synth.config(4, B=2, Nk=2, Nv=4, S=200, lens=[200, 77], base=719), 719, gates=True)
 
 
+def test_epilogue_prefill_whole_heads():
+    # 512 heads: the prefill takes whole-head workgroups before the epilogue
+    c = synth.config(4, B=8, Nk=16, Nv=64, S=130, lens=[130, 64, 1, 0, 99, 130, 128, 65], base=721)
+    _chunk(c, 721)
+
+
 def test_epilogue_prefill_fp32():
     c = synth.prefill_case(B=2, Nk=1, Nv=2, S=100, Dk=32, Dv=32, dtype="f32", base=720, lens=[100, 37],
                            chunk=32, scale=0.3, init_std=0.1)
