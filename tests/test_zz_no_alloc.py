@@ -1,8 +1,8 @@
 """GPU test of gdr_chunk_noalloc, the allocation-free entry point: its
 outputs and final states equal gdr_chunk's (the same kernels, the scratch
 taken from the library's fixed per-GPU array instead of a workspace), on two
-calls in a row, the second with a smaller input, so that whatever the first
-call left in the array cannot leak into the second's results."""
+calls in a row and more, each smaller than the first, so that whatever an
+earlier call left in the array cannot leak into a later call's results."""
 import pytest
 import torch
 
@@ -31,6 +31,8 @@ def test_noalloc_equals_chunk_twice_shrinking():
     # first the largest call the array holds (the chunked prefill workload's
     # 8192 chunks), then a smaller ragged one
     _both(synth.config(4, base=471))
+    # 512 heads take the whole-head workgroups (2560 chunks)
+    _both(synth.config(4, B=8, Nk=16, Nv=64, S=300, lens=[300, 131, 64, 1, 0, 299, 77, 200], base=474))
     _both(synth.config(4, B=2, Nk=2, Nv=4, S=300, lens=[300, 131], base=472))
 
 
