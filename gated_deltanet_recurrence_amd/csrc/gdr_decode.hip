@@ -212,34 +212,41 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 // Decode step with one token per sequence (S = 1), 16-bit I/O (bf16 or fp16),
 // Dk = Dv = 128.
 //
-// A workgroup of eight wavefronts updates one head at a time and walks the
-// heads g, g + G, g + 2G, ... (G workgroups, persistent). Wave j owns the
-// 16 rows [16j, 16j + 16) of the head's 128 x 128 state; lane l of it holds
-// columns 8 (l % 16) .. + 7 of the four consecutive rows 16j + 4 (l / 16) + i,
-// so each load or store instruction of the wave moves four whole 256-byte
-// rows and the wave as a whole a contiguous 4 KiB block. The column sums
-// S^T (D k) and S^T (D q) are reduced over the wave's four lane rows with the
-// cross-row lane swaps (v_permlane32_swap / v_permlane16_swap), then over the
-// eight waves through LDS with one barrier per head. All loads of the next
-// head (state, k, q, v, gk) are in flight while the current head is updated
-// and stored; its scalars are read one head earlier still. Every load goes
-// through a buffer resource whose size is zero when there is nothing to read,
-// so no load sits under a branch.
+// A workgroup of four wavefronts updates one head at a time and walks the
+// heads g, g + G, g + 2G, ... (G workgroups, persistent: three per CU). Wave j
+// owns the 32 rows [32j, 32j + 32) of the head's 128 x 128 state; lane l of it
+// holds columns 8 (l % 16) .. + 7 of the eight consecutive rows
+// 32j + 8 (l / 16) + i, so each load or store instruction of the wave moves
+// four whole 256-byte rows. The column sums S^T (D k) and S^T (D q) are
+// reduced over the wave's four lane rows with the cross-row lane swaps
+// (v_permlane32_swap / v_permlane16_swap), then over the four waves through
+// LDS with one barrier per head. All loads of the next head (state, k, q, v,
+// gk) are in flight while the current head is updated and stored; its scalars
+// are read one head earlier still. Every load goes through a buffer resource
+// whose size is zero when there is nothing to read, so no load sits under a
+// branch.
+//
+// Layout, measured on the decode step workload (2048 heads): eight waves per
+// head (four rows per lane), one workgroup per CU and the loads of two heads
+// ahead in flight took 25.7 us; four waves per head, three workgroups per CU
+// and one head ahead 24.5-24.7 us (two or four workgroups per CU: 25.8 and
+// 25.2 us; workgroup counts that leave CUs unevenly loaded: 26.7-28.0 us).
 //
 // With one token the output needs no pass over the updated state:
 //   S' = D S + k delta^T,  D = diag(exp(g) exp(gk_i)),  delta = beta (v - S^T D k)
 //   o  = scale S'^T q = scale (S^T (D q) + delta (k . q))
 namespace s1 {
 constexpr int DK = 128, DV = 128;
-constexpr int NW = 8;                 // waves per head (workgroup size 512)
-constexpr int RW = DK / NW;           // 16 rows per wave
-constexpr int NI = RW / 4;            // 4 rows per lane, one per instruction
-#ifndef GDR_S1_GROUPS
-#define GDR_S1_GROUPS 256
+#ifndef GDR_S1_NW
+#define GDR_S1_NW 4
 #endif
-constexpr int GROUPS = GDR_S1_GROUPS; // persistent workgroups
+constexpr int NW = GDR_S1_NW;         // waves per head (workgroup size 64 NW)
+constexpr int RW = DK / NW;           // rows per wave
+constexpr int NI = RW / 4;            // rows per lane, one per instruction
+static_assert(NI == 4 || NI == 8, "4 or 8 rows per lane");
+constexpr int PER_CU = 3;             // persistent workgroups per CU
 #ifndef GDR_S1_NB
-#define GDR_S1_NB 3
+#define GDR_S1_NB 2
 #endif
 constexpr int NB = GDR_S1_NB;         // heads whose loads are in flight
 }  // namespace s1
@@ -252,9 +259,10 @@ struct S1Head {
     int b, h, r;
     float beta, g;
     u32x4_t st[s1::NI];   // 8 16-bit columns of each of the lane's rows
-    u32x2_t k, q;         // the lane's 4 rows of k and q (16-bit)
+    u32x2_t k, q;         // the lane's first 4 rows of k and q (16-bit)
+    u32x2_t k2, q2;       // rows 4-7 with 8 rows per lane
     u32x4_t v;            // the lane's 8 columns of v (16-bit)
-    u32x4_t gk;           // the lane's 4 rows of gk (f32)
+    u32x4_t gk[s1::NI / 4];   // the lane's rows of gk (f32)
     uint32_t z;           // the epilogue's z at the lane's two output columns (16-bit)
 };
 
@@ -330,7 +338,8 @@ __device__ __forceinline__ void s1_barrier()
 // kernel from the logits and the raw gate input a. QN: q and k normalised in
 // the kernel. NRM: gated RMSNorm epilogue on the outputs (norm_pair).
 template <typename EL, bool GK, bool FG, bool QN, bool NRM>
-__global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, int nheads)
+__global__ __launch_bounds__(64 * s1::NW) __attribute__((amdgpu_waves_per_eu(s1::PER_CU * s1::NW / 4)))
+void decode_s1_kernel(DecodeParams p, int nheads)
 {
     using namespace s1;
     __shared__ float4 red[2][NW][64];
@@ -401,11 +410,22 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
             H.st[i] = __builtin_amdgcn_raw_buffer_load_b128(srs, ((row0 + i) * DV + cg * 8) * 2, 0, STREAM);
         const size_t qk = (size_t)H.b * p.Nk + H.h / rep;
         const int tb = on ? DK * 2 : 0;
-        H.k = __builtin_amdgcn_raw_buffer_load_b64(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
-        H.q = __builtin_amdgcn_raw_buffer_load_b64(brsrc(q + qk * DK, tb), row0 * 2, 0, 0);
+        if constexpr (NI == 4) {
+            H.k = __builtin_amdgcn_raw_buffer_load_b64(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
+            H.q = __builtin_amdgcn_raw_buffer_load_b64(brsrc(q + qk * DK, tb), row0 * 2, 0, 0);
+        } else {
+            const u32x4_t k4 = __builtin_amdgcn_raw_buffer_load_b128(brsrc(k + qk * DK, tb), row0 * 2, 0, 0);
+            const u32x4_t q4 = __builtin_amdgcn_raw_buffer_load_b128(brsrc(q + qk * DK, tb), row0 * 2, 0, 0);
+            H.k = u32x2_t{k4.x, k4.y};
+            H.k2 = u32x2_t{k4.z, k4.w};
+            H.q = u32x2_t{q4.x, q4.y};
+            H.q2 = u32x2_t{q4.z, q4.w};
+        }
         H.v = __builtin_amdgcn_raw_buffer_load_b128(brsrc(v + (size_t)vh * DV, on ? DV * 2 : 0), cg * 16, 0, 0);
         if constexpr (GK)
-            H.gk = __builtin_amdgcn_raw_buffer_load_b128(brsrc(p.gk + (size_t)vh * DK, on ? DK * 4 : 0), row0 * 4, 0, 0);
+#pragma unroll
+            for (int n = 0; n < NI / 4; ++n)
+                H.gk[n] = __builtin_amdgcn_raw_buffer_load_b128(brsrc(p.gk + (size_t)vh * DK, on ? DK * 4 : 0), (row0 + 4 * n) * 4, 0, 0);
         if constexpr (NRM)
             H.z = __builtin_amdgcn_raw_buffer_load_b32(brsrc(zsrc + (size_t)vh * DV, on ? DV * 2 : 0), (cg * 8 + lr * 2) * 2, 0, 0);
     };
@@ -417,7 +437,7 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         if constexpr (NRM) x ^= H.z;
 #pragma unroll
         for (int i = 0; i < NI; ++i) x ^= H.st[i].x ^ H.st[i].w;
-        if constexpr (GK) x ^= H.gk.x;
+        if constexpr (GK) x ^= H.gk[0].x;
         asm volatile("" ::"v"(x));
     };
     // Output columns of this lane in the writing wave: 8 cg + 2 lr, + 1.
@@ -434,15 +454,24 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         const float a = __expf(H.g);
         float dd[NI];
         if constexpr (GK) {
-            dd[0] = a * __expf(__uint_as_float(H.gk.x));
-            dd[1] = a * __expf(__uint_as_float(H.gk.y));
-            dd[2] = a * __expf(__uint_as_float(H.gk.z));
-            dd[3] = a * __expf(__uint_as_float(H.gk.w));
+#pragma unroll
+            for (int n = 0; n < NI / 4; ++n) {
+                dd[4 * n] = a * __expf(__uint_as_float(H.gk[n].x));
+                dd[4 * n + 1] = a * __expf(__uint_as_float(H.gk[n].y));
+                dd[4 * n + 2] = a * __expf(__uint_as_float(H.gk[n].z));
+                dd[4 * n + 3] = a * __expf(__uint_as_float(H.gk[n].w));
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < NI; ++i) dd[i] = a;
         }
-        const float kr[NI] = {EL::lo(H.k.x), EL::hi(H.k.x), EL::lo(H.k.y), EL::hi(H.k.y)};
+        // k and q of the lane's rows, as 16-bit pairs (rows 2pr, 2pr + 1)
+        uint32_t kp[NI / 2], qp[NI / 2];
+        kp[0] = H.k.x; kp[1] = H.k.y; qp[0] = H.q.x; qp[1] = H.q.y;
+        if constexpr (NI == 8) { kp[2] = H.k2.x; kp[3] = H.k2.y; qp[2] = H.q2.x; qp[3] = H.q2.y; }
+        float kr[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) kr[i] = (i & 1) ? EL::hi(kp[i >> 1]) : EL::lo(kp[i >> 1]);
         // Partial S^T (D k) and S^T (D q) over the lane's rows.
         uint32_t sw[NI][4];
         float kv[8], sq[8], kq = 0.f;
@@ -451,7 +480,9 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
 #pragma unroll
         for (int i = 0; i < NI; ++i) { sw[i][0] = H.st[i].x; sw[i][1] = H.st[i].y; sw[i][2] = H.st[i].z; sw[i][3] = H.st[i].w; }
         if constexpr (GK) {
-            const float qr[NI] = {EL::lo(H.q.x), EL::hi(H.q.x), EL::lo(H.q.y), EL::hi(H.q.y)};
+            float qr[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) qr[i] = (i & 1) ? EL::hi(qp[i >> 1]) : EL::lo(qp[i >> 1]);
             float dk[NI], dq[NI];
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
@@ -471,9 +502,8 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
             // One decay for all rows: the sums run over 16-bit pairs of rows
             // (v_dot2_f32_bf16 / v_dot2_f32_f16, exact products) and take
             // exp(g) afterwards.
-            const uint32_t kp[2] = {H.k.x, H.k.y}, qp[2] = {H.q.x, H.q.y};
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
+            for (int pr = 0; pr < NI / 2; ++pr) {
                 const uint32_t kb = kp[pr], qb = qp[pr];
                 kq = EL::dot2(kb, qb, kq);
 #pragma unroll
@@ -498,11 +528,11 @@ __global__ __launch_bounds__(64 * s1::NW) void decode_s1_kernel(DecodeParams p, 
         // |k|^2 and |q|^2 for the in-kernel normalisation.
         float kk = 0.f, qq = 0.f;
         if constexpr (QN) {
-            const float qr[NI] = {EL::lo(H.q.x), EL::hi(H.q.x), EL::lo(H.q.y), EL::hi(H.q.y)};
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
+                const float qi = (i & 1) ? EL::hi(qp[i >> 1]) : EL::lo(qp[i >> 1]);
                 kk = fmaf(kr[i], kr[i], kk);
-                qq = fmaf(qr[i], qr[i], qq);
+                qq = fmaf(qi, qi, qq);
             }
             kk = rows_sum(kk);
             qq = rows_sum(qq);
@@ -930,7 +960,11 @@ hipError_t launch_decode(int dtype, int Dk, int Dv, const DecodeParams &p, hipSt
         *supported = true;
         *norm_done = true;
         const int nheads = p.B * p.Nv;
-        const dim3 grid((unsigned)(nheads < s1::GROUPS ? nheads : s1::GROUPS)), block(64 * s1::NW);
+        int dev = 0, ncu = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0) ncu = 256;
+        const int groups = s1::PER_CU * ncu;
+        const dim3 grid((unsigned)(nheads < groups ? nheads : groups)), block(64 * s1::NW);
         DecodeParams pc = p;
         int nh = nheads;
         void *args[] = {&pc, &nh};
