@@ -22,10 +22,11 @@
 // Kernels:
 //  * chunk_t_kernel + chunk_mfma_kernel — bf16 or fp16 I/O, Dk = Dv = 128, C = 64.
 //    chunk_t_kernel forms T = (I + A)^-1 of every chunk of every sequence in
-//    parallel (it depends on k, beta and g only) into the caller's workspace;
-//    chunk_mfma_kernel then makes one pass over the chunks per (sequence,
-//    value head, 64-column tile of Dv), carrying its slice of the state in
-//    float32 matrix-core accumulators. All dense products run on
+//    parallel (it depends on k, beta and g only) into the caller's workspace,
+//    and writes the output rows of chunks wholly past a sequence's length as
+//    zeros; chunk_mfma_kernel then makes one pass over the chunks per
+//    (sequence, value head, half or whole of Dv), carrying its slice of the
+//    state in float32 matrix-core accumulators. All dense products run on
 //    v_mfma_f32_32x32x16_bf16 (v_mfma_f32_32x32x16_f16 for fp16 I/O) with
 //    operands in the I/O format.
 //  * chunk_f32_kernel — float32 I/O, small heads. The same chunk algorithm in
