@@ -1305,9 +1305,14 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkParams p)
     for (int e = nchunks * C * D + tid; e < Sl * D; e += 256) ob[e] = 0.f;
 }
 
+// The 16-bit matrix-core path takes chunk sizes 16, 32 and 64 and computes in
+// chunks of 64: the chunk size is a blocking of the same recurrence, and the
+// result differs only in rounding.
+static bool mfma_chunk_size(int C) { return C == 16 || C == 32 || C == mk::C; }
+
 int64_t chunk_workspace_bytes(int dtype, int Dk, int Dv, int C, int B, int Nv, int S)
 {
-    if ((dtype == 1 || dtype == 2) && Dk == mk::DK && Dv == mk::DV && C == mk::C)
+    if ((dtype == 1 || dtype == 2) && Dk == mk::DK && Dv == mk::DV && mfma_chunk_size(C))
         return (int64_t)B * Nv * ((S + mk::C - 1) / mk::C) * tk::CHUNK_ELEMS * 2;
     return 0;
 }
@@ -1329,7 +1334,7 @@ hipError_t launch_chunk(int dtype, int Dk, int Dv, int C, const ChunkParams &p, 
     *supported = true;
     ChunkParams pc = p;
     if (dtype == 1 || dtype == 2) {
-        if (Dk == mk::DK && Dv == mk::DV && C == mk::C) {
+        if (Dk == mk::DK && Dv == mk::DV && mfma_chunk_size(C)) {
             const bool half = dtype == 2;
             // T of every chunk first, then the pass over the chunks.
             int nchk = (p.S + mk::C - 1) / mk::C;

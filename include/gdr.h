@@ -193,9 +193,11 @@ GDR_API gdr_status gdr_decode(const gdr_decode_args *a, void *stream);
  * Inputs at positions t >= L_b are never read.
  * The result equals the token-by-token recurrence up to rounding; the state
  * is carried in float32 between chunks.
- * Supported: bf16 or fp16 with Dk = Dv = 128 and chunk_size 64 (matrix-core
- *   path, which first forms (I + A)^-1 of every chunk in the workspace:
- *   B * Nv * ceil(S / 64) * 6144 bytes); f32 with Dk = Dv in {16, 32} and
+ * Supported: bf16 or fp16 with Dk = Dv = 128 and chunk_size 16, 32 or 64
+ *   (matrix-core path, which computes in chunks of 64 whatever the chunk
+ *   size: a chunk size is a blocking of the same recurrence and changes only
+ *   rounding; it first forms (I + A)^-1 of every chunk of 64 in the
+ *   workspace: B * Nv * ceil(S / 64) * 6144 bytes); f32 with Dk = Dv in {16, 32} and
  *   chunk_size in {16, 32, 64}, or Dk = Dv = 64 and chunk_size in {16, 32}
  *   (no workspace).
  * Errors: GDR_ERR_NULL if a, q, k, v, out or final_state is NULL, beta is

@@ -149,7 +149,8 @@ def test_decode_validation(lib, kw, code):
     (dict(k=None), gdr.GDR_ERR_NULL),
     (dict(final_state=None), gdr.GDR_ERR_NULL),
     (dict(Dk=64, Dv=64), gdr.GDR_ERR_UNSUPPORTED),
-    (dict(chunk_size=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(chunk_size=48), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(chunk_size=128), gdr.GDR_ERR_UNSUPPORTED),
     (dict(dtype=gdr.GDR_F32, Dk=128, Dv=128), gdr.GDR_ERR_UNSUPPORTED),
     (dict(dtype=gdr.GDR_F32, Dk=64, Dv=64, chunk_size=64), gdr.GDR_ERR_UNSUPPORTED),
     (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
@@ -160,7 +161,7 @@ def test_decode_validation(lib, kw, code):
     (dict(B=0, q=None, out=None, workspace=None), gdr.GDR_OK),
     (dict(beta=None), gdr.GDR_ERR_NULL),
     (dict(dtype=3), gdr.GDR_ERR_DTYPE),
-    (dict(dtype=gdr.GDR_F16, chunk_size=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(dtype=gdr.GDR_F16, chunk_size=48), gdr.GDR_ERR_UNSUPPORTED),
     (dict(dtype=gdr.GDR_F16, Dk=64, Dv=64), gdr.GDR_ERR_UNSUPPORTED),
     (dict(dtype=gdr.GDR_F16, workspace=None), gdr.GDR_ERR_NULL),
 ] + _OPTION_CASES)
@@ -171,14 +172,14 @@ def test_chunk_validation(lib, kw, code):
 
 # The allocation-free entry point validates like gdr_chunk, ignores the
 # workspace fields, and refuses calls whose scratch exceeds its fixed array
-# (B * Nv * ceil(S / 64) chunks of 6 KiB on the bf16 path) before touching
+# (B * Nv * ceil(S / 64) chunks of 6 KiB on the 16-bit path) before touching
 # the device. Calls that pass validation are GPU tests.
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=-1), gdr.GDR_ERR_DTYPE),
     (dict(Nv=5), gdr.GDR_ERR_SHAPE),
     (dict(k=None), gdr.GDR_ERR_NULL),
     (dict(beta=None), gdr.GDR_ERR_NULL),
-    (dict(chunk_size=32), gdr.GDR_ERR_UNSUPPORTED),
+    (dict(chunk_size=48), gdr.GDR_ERR_UNSUPPORTED),
     (dict(initial_state=FAKE + 8), gdr.GDR_ERR_UNSUPPORTED),
     (dict(B=0, q=None, out=None), gdr.GDR_OK),
     (dict(B=4, Nk=16, Nv=32, S=4097), gdr.GDR_ERR_SCRATCH_LIMIT),
@@ -284,11 +285,15 @@ def test_binding_maps_status_to_exceptions(lib):
 
 
 def test_chunk_workspace_size(lib):
-    # The matrix-core path needs 8 KB per (sequence, value head, chunk of 64);
-    # the float32 path needs none.
+    # The matrix-core path needs 6 KB per (sequence, value head, chunk of 64),
+    # for chunk sizes 16 and 32 too (it computes in chunks of 64); the float32
+    # path needs none.
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk())) == 2 * 4 * 2 * 6144
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=128))) == 2 * 4 * 2 * 6144
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(S=0))) == 0
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F32, Dk=32, Dv=32, chunk_size=32))) == 0
     assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(dtype=gdr.GDR_F16))) == 2 * 4 * 2 * 6144
+    for cs in (16, 32):
+        assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(chunk_size=cs))) == 2 * 4 * 2 * 6144
+    assert lib.gdr_chunk_workspace_size(ctypes.byref(_chk(chunk_size=48))) == 0
     assert lib.gdr_chunk_workspace_size(None) == -1

@@ -116,6 +116,16 @@ def test_whole_heads_agree_with_column_halves():
     assert_zero_rows(o_all, c.valid_lengths())
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_16_bit_chunk_sizes_16_and_32(chunk, dtype):
+    # the 16-bit path takes chunk sizes 16 and 32 and computes in chunks of
+    # 64: a blocking of the same recurrence, so the oracle's results hold
+    c = synth.config(4, B=2, Nk=2, Nv=4, S=300, lens=[300, 201], base=420 + chunk, chunk=chunk, dtype=dtype)
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
 def test_nan_in_padding_is_never_read():
     c = synth.config(4, B=3, Nk=1, Nv=2, S=200, lens=[200, 130, 1], base=416, poison_pad=True)
     out, fin = run_chunk(c)
