@@ -775,7 +775,7 @@ __global__ __launch_bounds__(mk::NTHR) void chunk_mfma_kernel(ChunkParams p, int
         // With column halves the recurrence is the critical path: its
         // instructions win issue arbitration against the prep waves sharing
         // the SIMD. With whole heads every SIMD holds a chain wave and a prep
-        // wave, the prep's path is the longer one, and equal priority measured
+        // wave, the two paths are about as long, and equal priority measured
         // best (varlen prefill pass 1330 us, against 1411 with the chain
         // raised by one and 1429 by two).
         if constexpr (NT == 2) __builtin_amdgcn_s_setprio(2);
