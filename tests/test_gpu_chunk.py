@@ -174,6 +174,16 @@ def test_decay_extremes(gate):
     _check_full(c, out, fin)
 
 
+@pytest.mark.parametrize("B,Nk,Nv", [(4, 40, 40), (3, 8, 64)])
+def test_whole_heads_head_grouping(B, Nk, Nv):
+    # whole-head workgroups (over 128 heads) with one value head per key head,
+    # and eight: the groups kept on one XCD are 1 and 8 units wide
+    c = synth.config(4, B=B, Nk=Nk, Nv=Nv, S=130, lens=[130, 64, 1, 0][:B], base=445 + Nv)
+    assert c.B * c.Nv > 128
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
 @pytest.mark.parametrize("Nk,Nv", [(3, 3), (1, 8)])
 def test_head_grouping(Nk, Nv):
     # one value head per key head, and eight: the workgroup groups that share
