@@ -89,7 +89,7 @@ gdr_status check_conv(const Args *a, int max_S)
     const int64_t C = 2LL * a->Nk * a->Dk + (int64_t)a->Nv * a->Dv;
     // 32-bit channel and grid arithmetic; 64-bit element offsets
     // 32-bit byte offsets within one sequence's inputs and one head's plane
-    // (the prefill reads whole 64-token blocks, up to S + 63)
+    // (the prefill reads whole token blocks of at most 64, up to S + 63)
     if (C > (1LL << 30) || a->B > 65535 || ((int64_t)a->S + 64) * C * (a->dtype == GDR_F32 ? 4 : 2) > 0x7fffffffLL)
         return GDR_ERR_UNSUPPORTED;
     if (!aligned16(a->x) || !aligned16(a->q) || !aligned16(a->k) || !aligned16(a->v) || !aligned4(a->weight) ||

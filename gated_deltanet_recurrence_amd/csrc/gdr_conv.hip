@@ -21,8 +21,8 @@ namespace gdr {
 namespace {
 
 constexpr int CONV_THREADS = 256;
-constexpr int CONV_TB = 64;    // tokens per prefill workgroup
-constexpr int CONV_AHEAD = 8;  // input loads issued ahead of their use
+constexpr int CONV_TB = 32;    // tokens per prefill workgroup
+constexpr int CONV_AHEAD = 16; // input loads issued ahead of their use
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -31,9 +31,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t conv_rsrc(const void *p, int64
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// Two adjacent channels through a bounded buffer resource (byte offset off):
-// reads past the bound return zeros, stores past it are dropped, so neither
-// needs a branch.
+// Two adjacent channels: loads through a bounded buffer resource (byte offset
+// off; reads past the bound return zeros, so they need no branch), stores
+// through a plain pointer, since the destination plane differs between lanes
+// on either side of a head boundary and a buffer resource must be uniform over
+// the wave. store_nt carries the non-temporal hint, for the prefill's
+// outputs: each is written once and read by a later kernel, and together
+// they outgrow the L2.
 template <typename T> struct Pair2;
 template <typename T> struct Pair16 {
     typedef typename Elem<T>::type EL;
@@ -42,9 +46,10 @@ template <typename T> struct Pair16 {
         const uint32_t u = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
         return make_float2(EL::lo(u), EL::hi(u));
     }
-    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float2 v)
+    static __device__ __forceinline__ void store(T *p, float2 v) { *reinterpret_cast<uint32_t *>(p) = EL::pack(v.x, v.y); }
+    static __device__ __forceinline__ void store_nt(T *p, float2 v)
     {
-        __builtin_amdgcn_raw_buffer_store_b32(EL::pack(v.x, v.y), r, off, 0, 0);
+        __builtin_nontemporal_store(EL::pack(v.x, v.y), reinterpret_cast<uint32_t *>(p));
     }
     static __device__ __forceinline__ float one(const T *p) { return to_f32(*p); }
     static __device__ __forceinline__ void put(T *p, float v) { *p = from_f32<T>(v); }
@@ -57,9 +62,10 @@ template <> struct Pair2<float> {
         const u32x2_t u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
         return make_float2(__uint_as_float(u.x), __uint_as_float(u.y));
     }
-    static __device__ __forceinline__ void store(__amdgpu_buffer_rsrc_t r, int off, float2 v)
+    static __device__ __forceinline__ void store(float *p, float2 v) { *reinterpret_cast<float2 *>(p) = v; }
+    static __device__ __forceinline__ void store_nt(float *p, float2 v)
     {
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(v.x), __float_as_uint(v.y)}, r, off, 0, 0);
+        __builtin_nontemporal_store(u32x2_t{__float_as_uint(v.x), __float_as_uint(v.y)}, reinterpret_cast<u32x2_t *>(p));
     }
     static __device__ __forceinline__ float one(const float *p) { return *p; }
     static __device__ __forceinline__ void put(float *p, float v) { *p = v; }
@@ -88,7 +94,9 @@ __device__ __forceinline__ T *split_dst(const ConvParams &p, int b, int c, int &
     return static_cast<T *>(p.v) + ((size_t)b * p.Nv + c / p.Dv) * p.S * p.Dv;
 }
 
-__device__ __forceinline__ float conv_silu(float u) { return u / (1.f + __expf(-u)); }
+// u sigmoid(u) with the hardware reciprocal (within 1 ulp) in place of a
+// division: 1 + e^-u is at least 1, and an infinite one gives u * 0.
+__device__ __forceinline__ float conv_silu(float u) { return u * __builtin_amdgcn_rcpf(1.f + __expf(-u)); }
 
 // One token: window win[0..K-2] (oldest first) and input xin; returns y and
 // shifts xin into the window.
@@ -120,9 +128,9 @@ __device__ __forceinline__ void conv_weights(const ConvParams &p, int c, float (
 }
 
 // Workgroup (channel pairs x, token block y, sequence z). Inputs are read
-// through a resource bounded by the sequence's valid tokens and outputs
-// written through one bounded by the head's plane: every token of the block
-// is loaded ahead and stored (zeros at t >= L) with no branch.
+// through a resource bounded by the sequence's valid tokens: every token of
+// the block is loaded ahead with no branch, and stored (zeros at t >= L) when
+// it lies in the plane's S rows.
 template <typename T, int K>
 __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p)
 {
@@ -147,8 +155,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p
     float2 bv;
     conv_weights<K>(p, c, w0, w1, bv);
     int D, d;
-    T *plane = split_dst<T>(p, b, c, D, d);
-    const auto ors = conv_rsrc(plane, (int64_t)p.S * D * E);
+    T *const out = split_dst<T>(p, b, c, D, d) + d;
     float2 win[KW];
 #pragma unroll
     for (int j = 0; j + 1 < K; ++j) win[j] = input(t0 - (K - 1) + j);
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvParams p
         for (int i = 0; i < CONV_AHEAD; ++i) {
             float2 y = conv_step<K>(win, xs[nb & 1][i], w0, w1, bv);
             if (ta + i >= L) y = make_float2(0.f, 0.f);   // rows past the length: exact zeros
-            Pair2<T>::store(ors, ((ta + i) * D + d) * E, y);
+            if (ta + i < p.S) Pair2<T>::store_nt(out + (size_t)(ta + i) * D, y);
         }
     }
     // The final state (the last K - 1 inputs) is written by the first token
@@ -214,8 +221,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvParams p)
     float2 bv;
     conv_weights<K>(p, c, w0, w1, bv);
     int D, d;
-    T *plane = split_dst<T>(p, b, c, D, d);
-    const auto ors = conv_rsrc(plane, (int64_t)S * D * E);
+    T *const out = split_dst<T>(p, b, c, D, d) + d;
     float2 win[KW];
     if (L > 0) {
         const T *src = pool + ((size_t)r * C + c) * (K - 1);
@@ -226,10 +232,10 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvParams p)
     for (int t = 0; t < 8; ++t) {
         if (t >= S) break;
         if (t >= L) {
-            Pair2<T>::store(ors, (t * D + d) * E, make_float2(0.f, 0.f));
+            Pair2<T>::store(out + (size_t)t * D, make_float2(0.f, 0.f));
             continue;
         }
-        Pair2<T>::store(ors, (t * D + d) * E, conv_step<K>(win, xs[t], w0, w1, bv));
+        Pair2<T>::store(out + (size_t)t * D, conv_step<K>(win, xs[t], w0, w1, bv));
         const int s = ld_const(p.idx, (size_t)b * S + t);
         const bool again = t + 1 < L && ld_const(p.idx, (size_t)b * S + t + 1) == s;
         if (K > 1 && s >= 0 && s < p.slots && !again) {

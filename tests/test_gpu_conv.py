@@ -65,9 +65,16 @@ def test_conv_prefill_fp32_and_taps():
 
 
 def test_conv_prefill_pair_kernel():
-    # head sizes even but not multiples of 8: two channels per thread
+    # head sizes even but not multiples of 8: the waves' lanes straddle head
+    # boundaries, so one store instruction writes to several planes
     _prefill(2, 150, (1, 10, 2, 6), 3, "f32", 817, lens=[150, 65])
     _prefill(2, 80, (2, 6, 2, 10), 4, "bf16", 818, lens=[80, 1])
+
+
+def test_conv_prefill_mixed_head_sizes():
+    # key and value heads of different sizes, in bf16 and fp16, with K = 4 and 2
+    _prefill(2, 97, (1, 12, 3, 20), 4, "bf16", 819, lens=[97, 33])
+    _prefill(2, 66, (2, 4, 2, 12), 2, "f16", 820, lens=[3, 66])
 
 
 def test_conv_prefill_no_state_no_bias_and_alias():
