@@ -77,6 +77,47 @@ def test_conv_prefill_mixed_head_sizes():
     _prefill(2, 66, (2, 4, 2, 12), 2, "f16", 820, lens=[3, 66])
 
 
+def test_conv_prefill_saturated_silu():
+    # Inputs and states scaled by 256 (exact in every format): pre-activations
+    # reach several hundred, beyond where e^-u is finite in float32, so SiLU
+    # must give u for large u and a zero for very negative u. The outputs are
+    # large, so the bar adds one rounding of the output (2^-8 |y| for bf16,
+    # 2^-24 for float32) and the float32 accumulation of the K taps
+    # (K 2^-23 (sum_j |w_j| max|x| + |bias|)) to the absolute bar.
+    heads = (1, 16, 2, 16)
+    Nk, Dk, Nv, Dv = heads
+    C, B, S, K = 2 * Nk * Dk + Nv * Dv, 2, 70, 4
+    for dtype, rel in (("bf16", 2.0 ** -8), ("f32", 2.0 ** -24)):
+        x, w, bb, st = synth.conv_inputs(831, B, S, C, K, dtype)
+        xs, ss = synth.widen(x, dtype) * 256.0, synth.widen(st, dtype) * 256.0
+        if dtype == "bf16":
+            x, st = synth.bf16_bits(xs), synth.bf16_bits(ss)
+        else:
+            x, st = xs.astype(np.float32), ss.astype(np.float32)
+        L = np.array([S, 41], np.int32)
+        say(f"gdr_conv_prefill {dtype} B={B} S={S} heads={heads} K={K}, inputs x256")
+        q, k, v, fin = gdr.gdr_conv_prefill(to_dev(x), to_dev(w), heads, bias=to_dev(bb), initial_state=to_dev(st),
+                                            actual_seq_lengths=to_dev(L))
+        torch.cuda.synchronize()
+        y_ref, f_ref = oracle_conv.prefill(synth.widen(x, dtype), w, bb, synth.widen(st, dtype), L)
+        m = max(float(np.abs(xs).max()), float(np.abs(ss).max()))
+        acc = K * 2.0 ** -23 * (np.abs(w).sum(1) * m + np.abs(bb))   # per channel
+        saturated = 0
+        for name, got, ref, a in zip(("q", "k", "v"), (q, k, v),
+                                     oracle_conv.split(y_ref, Nk, Dk, Nv, Dv),
+                                     oracle_conv.split(np.broadcast_to(acc, (1, 1, C)), Nk, Dk, Nv, Dv)):
+            g = to_f64(got)
+            for b in range(B):
+                n = int(L[b])
+                r = ref[b, :, :n]
+                bound = TOL[dtype] + rel * np.abs(r) + a[0]
+                assert np.all(np.abs(g[b, :, :n] - r) <= bound), f"{dtype} {name} b={b}"
+                saturated += int((np.abs(r) > 89.0).sum())
+                assert torch.all(raw_bits(got[b, :, n:]) == 0), f"{name} b={b}: nonzero rows past the length"
+        assert saturated > 0, "no pre-activation beyond the float32 range of e^-u"
+        assert np.array_equal(to_f64(fin), f_ref), "final state"
+
+
 def test_conv_prefill_no_state_no_bias_and_alias():
     _prefill(2, 130, (2, 64, 2, 64), 4, "bf16", 815, init=False, bias=False)
     _prefill(3, 90, (2, 64, 4, 64), 4, "bf16", 816, lens=[90, 2, 64], alias=True)
