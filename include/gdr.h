@@ -252,7 +252,8 @@ GDR_API gdr_status gdr_chunk(const gdr_chunk_args *a, void *stream);
  * straight into q (B, Nk, S, Dk), k (B, Nk, S, Dk) and v (B, Nv, S, Dv):
  * channel c < Nk*Dk is q[b, c / Dk, t, c % Dk], the next Nk*Dk are k likewise,
  * the rest v. Rows t >= L_b of q, k and v are written as exact zeros, and
- * x there is never read. The sums run in float32; outputs are rounded once.
+ * x there is never read. The sums run in float32, the SiLU's division as a
+ * hardware reciprocal (within 1 ulp of float32); outputs are rounded once.
  *
  * Sizes: B >= 0, S >= 1 (decode: S <= 8), Nk, Nv, Dk, Dv >= 1 with Nv % Nk == 0,
  *   Dk and Dv even, 1 <= K <= 8. Tensors (device, row-major, dtype as for the
