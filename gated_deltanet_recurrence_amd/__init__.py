@@ -191,7 +191,7 @@ def gdr_decode(q, k, v, beta, state_pool, actual_seq_lengths, ssm_state_indices,
     """Recurrent decode; updates state_pool in place. Returns (out, state_pool).
 
     q, k (B, Nk, S, Dk); v (B, Nv, S, Dv); beta (B, Nv, S); state_pool
-    (slots, Nv, Dk, Dv) — all of one dtype (bfloat16 or float32); g (B, Nv, S)
+    (slots, Nv, Dk, Dv) — all of one dtype (bfloat16, float16 or float32); g (B, Nv, S)
     and gk (B, Nv, S, Dk) float32 or None; actual_seq_lengths (B,),
     ssm_state_indices (B*S,), num_accepted_tokens (B,) or None — int32.
     gates: None, or (beta_logits, a, A_log, dt_bias) — logits and a (B, Nv, S)
