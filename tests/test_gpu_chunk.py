@@ -174,6 +174,30 @@ def test_decay_extremes(gate):
     _check_full(c, out, fin)
 
 
+def _degenerate(c, zero_keys):
+    """beta = 0 on even value heads (nothing written: the state only decays,
+    A = 0 and T = I) and beta = 1 on odd ones, and all-zero keys on the tokens
+    of zero_keys (their rows and columns of A vanish)."""
+    one = synth.bf16_bits(np.float32(1.0)) if c.dtype == "bf16" else np.asarray(1.0, c.beta.dtype)
+    c.beta = c.beta.copy()
+    c.beta[:, 0::2] = 0
+    c.beta[:, 1::2] = one
+    c.k = c.k.copy()
+    c.k[:, :, zero_keys] = 0
+    return c
+
+
+@pytest.mark.parametrize("Nk,Nv", [(1, 2), (16, 160)])
+def test_degenerate_betas_and_keys(Nk, Nv):
+    # column halves (2 heads) and whole heads (320 heads); the zero keys span
+    # the boundary between the first two chunks
+    c = _degenerate(synth.prefill_case(B=2, Nk=Nk, Nv=Nv, S=150, Dk=128, Dv=128, base=460 + Nv, init_std=0.05,
+                                       lens=[150, 97]), slice(40, 80))
+    say(f"gdr_chunk bf16 B=2 Nv={Nv} S=150: beta 0 / 1 by head, zero keys on tokens 40-79")
+    out, fin = run_chunk(c)
+    _check_full(c, out, fin)
+
+
 @pytest.mark.parametrize("B,Nk,Nv", [(4, 40, 40), (3, 8, 64)])
 def test_whole_heads_head_grouping(B, Nk, Nv):
     # whole-head workgroups (over 128 heads) with one value head per key head,

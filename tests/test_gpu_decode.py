@@ -168,6 +168,24 @@ def test_single_token_skipped_tiles_and_gates(gk):
     _check_decode(c, out, pool)
 
 
+@pytest.mark.parametrize("S", [1, 4])
+def test_degenerate_betas_and_keys(S):
+    # beta = 0 on even value heads (the state only decays) and 1 on odd ones,
+    # and all-zero keys for every token of every third sequence; the one-token
+    # kernel (S = 1) and the multi-token kernel (S = 4)
+    B = 24
+    c = synth.decode_case(B=B, Nk=4, Nv=16, S=S, Dk=128, Dv=128, slots=B * S + 5, base=4747 + S)
+    one = synth.bf16_bits(np.float32(1.0))
+    c.beta = c.beta.copy()
+    c.beta[:, 0::2] = 0
+    c.beta[:, 1::2] = one
+    c.k = c.k.copy()
+    c.k[0::3] = 0
+    say(f"decode bf16 B={B} S={S}: beta 0 / 1 by head, zero keys for every third sequence")
+    out, pool = run_decode(c)
+    _check_decode(c, out, pool)
+
+
 def test_single_token_many_heads_per_workgroup():
     # 97 * 32 = 3104 heads: twelve or thirteen per workgroup.
     c = synth.decode_case(B=97, Nk=8, Nv=32, S=1, Dk=128, Dv=128, slots=128, base=4343)
