@@ -187,13 +187,14 @@ def _degenerate(c, zero_keys):
     return c
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("Nk,Nv", [(1, 2), (16, 160)])
-def test_degenerate_betas_and_keys(Nk, Nv):
+def test_degenerate_betas_and_keys(Nk, Nv, dtype):
     # column halves (2 heads) and whole heads (320 heads); the zero keys span
     # the boundary between the first two chunks
-    c = _degenerate(synth.prefill_case(B=2, Nk=Nk, Nv=Nv, S=150, Dk=128, Dv=128, base=460 + Nv, init_std=0.05,
-                                       lens=[150, 97]), slice(40, 80))
-    say(f"gdr_chunk bf16 B=2 Nv={Nv} S=150: beta 0 / 1 by head, zero keys on tokens 40-79")
+    c = _degenerate(synth.prefill_case(B=2, Nk=Nk, Nv=Nv, S=150, Dk=128, Dv=128, dtype=dtype, base=460 + Nv,
+                                       init_std=0.05, lens=[150, 97]), slice(40, 80))
+    say(f"gdr_chunk {dtype} B=2 Nv={Nv} S=150: beta 0 / 1 by head, zero keys on tokens 40-79")
     out, fin = run_chunk(c)
     _check_full(c, out, fin)
 
